@@ -1,0 +1,147 @@
+"""CPU oracle for the guarded W8A8 block-quantized linear (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are its only users.  The GPU library never
+imports, links or calls it, and it shares no code with it.  The arithmetic
+lives in ``oracle.c`` (plain C, see its header for the passages it follows);
+this module only marshals numpy arrays.
+
+bf16 tensors are passed as ``uint16`` bit patterns, quantized tensors as
+``int8``, scales as ``float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+DTYPE_BF16, DTYPE_FP16, DTYPE_FP32 = 0, 1, 2
+PATH_INT8, PATH_BF16 = 0, 1
+BLOCK = 128
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python oracle/build.py")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_quantize_block.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_kblock_partials.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P]
+        L.oracle_linear_int8_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+        L.oracle_linear_bf16_rows.argtypes = [_P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
+        L.oracle_route.argtypes = [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int]
+        L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        L.oracle_fp16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_fp16_to_f64.restype = ctypes.c_double
+        L.oracle_gelu_bf16.argtypes = [_P, _I64, _P]
+        for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
+                  "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
+                  "oracle_num_threads"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def quantize_block(x_bf16: np.ndarray):
+    """128x128 block-absmax INT8 quantization -> (q int8 [R,C], s fp32 [R/128, C/128])."""
+    x = _c(x_bf16, np.uint16)
+    r, c = x.shape
+    q = np.empty((r, c), np.int8)
+    s = np.empty((max(r // BLOCK, 1), max(c // BLOCK, 1)), np.float32)
+    _check(lib().oracle_quantize_block(_ptr(x), r, c, _ptr(q), _ptr(s)), "quantize_block")
+    return q, s
+
+
+def kblock_partials(qx, qw, m0=0, mt=None, n0=0, nt=None):
+    """int32 per-K-block partial sums, shape [mt, nt, K/128]."""
+    qx = _c(qx, np.int8)
+    qw = _c(qw, np.int8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    mt = M - m0 if mt is None else mt
+    nt = N - n0 if nt is None else nt
+    out = np.empty((mt, nt, K // BLOCK), np.int32)
+    _check(lib().oracle_kblock_partials(_ptr(qx), _ptr(qw), M, N, K, m0, mt, n0, nt, _ptr(out)),
+           "kblock_partials")
+    return out
+
+
+def linear_int8(qx, sx, qw, sw, bias=None, rows=None, want_f64=False):
+    """Dequantized bf16 output for the given rows (all rows if None)."""
+    qx = _c(qx, np.int8)
+    qw = _c(qw, np.int8)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    b = None if bias is None else _c(bias, np.uint16)
+    M, K = qx.shape
+    N = qw.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    nr = M if r is None else r.shape[0]
+    y = np.empty((nr, N), np.uint16)
+    y64 = np.empty((nr, N), np.float64) if want_f64 else None
+    _check(lib().oracle_linear_int8_rows(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(b), M, N, K,
+                                         _ptr(r), nr, _ptr(y), _ptr(y64)), "linear_int8")
+    return (y, y64) if want_f64 else y
+
+
+def linear_bf16(x, x_dtype, w_bf16, bias=None, rows=None):
+    """bf16 fallback linear; x is uint16 bits (bf16/fp16) or float32."""
+    xd = {DTYPE_BF16: np.uint16, DTYPE_FP16: np.uint16, DTYPE_FP32: np.float32}[x_dtype]
+    x = _c(x, xd)
+    w = _c(w_bf16, np.uint16)
+    b = None if bias is None else _c(bias, np.uint16)
+    M, K = x.shape
+    N = w.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    nr = M if r is None else r.shape[0]
+    y = np.empty((nr, N), np.uint16)
+    _check(lib().oracle_linear_bf16_rows(_ptr(x), x_dtype, _ptr(w), _ptr(b), M, N, K, _ptr(r), nr,
+                                         _ptr(y)), "linear_bf16")
+    return y
+
+
+def route(x_dtype, M, K, N, has_qweight):
+    return lib().oracle_route(x_dtype, M, K, N, int(bool(has_qweight)))
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(lib().oracle_f64_to_bf16(float(v)))
+
+
+def fp16_to_f64(h: int) -> float:
+    return float(lib().oracle_fp16_to_f64(int(h)))
+
+
+def gelu_bf16(x_bf16):
+    x = _c(x_bf16, np.uint16)
+    y = np.empty_like(x)
+    _check(lib().oracle_gelu_bf16(_ptr(x), x.size, _ptr(y)), "gelu_bf16")
+    return y

@@ -1,0 +1,279 @@
+/*
+ * CPU oracle for the guarded W8A8 block-quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing but the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load or call this library.  It shares
+ * no code, header, table or helper with the GPU library; it is plain, slow,
+ * obviously-correct C (gcc -O2, no fast-math, no FP contraction) with OpenMP
+ * over independent blocks or rows only.
+ *
+ * What it computes, and where the pages say so:
+ *   - 128x128 block granularity for weights and activations:
+ *       TurboDiffusion news article (bjdmk.com.cn), section on sparsity,
+ *       distillation and full-pipeline quantization, and its inference list
+ *       (weights of linear layers to INT8 per 128x128 block; activations at
+ *       the same block granularity at inference, run on INT8 tensor cores).
+ *   - scale = max-abs / 127, static weights, dynamic activations, INT32
+ *       accumulation, scales applied in the epilogue, optional bias:
+ *       TurboT2VA paper (arXiv 2608.24674), architecture-aware inference
+ *       stack, W8A8 linear paragraph.  (There it is stated per row / per
+ *       output channel; the block form takes the same rule per block.)
+ *   - the guard (bf16 input, M, K, N multiples of 128, else a bf16 linear on
+ *       the retained bf16 weight): TurboT2VA paper, same section, guard
+ *       paragraph; pchao.org summary of TurboT2VA, method overview and
+ *       caveats lists.
+ *
+ * Readings taken where the pages are silent (each also listed with the
+ * design notes): correctly rounded fp32 division x/s; rint half-to-even;
+ * clamp to [-127, 127]; an all-zero block has s = 0 and q = 0 (no epsilon
+ * floor); fp32 scales stored row-major [rows/128, K/128]; exact int32 sum per
+ * 128-deep K-block, fp64 accumulation across K-blocks, one rounding fp64 ->
+ * bf16 (nearest, ties to even); non-bf16 inputs of the fallback are first
+ * rounded to bf16.
+ *
+ * Parity pins: every function here is pinned by the CPU tests against
+ * hand-computed examples, closed forms, invariants or brute force; none is
+ * "parity unpinned".
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BLOCK 128
+
+enum { OR_DTYPE_BF16 = 0, OR_DTYPE_FP16 = 1, OR_DTYPE_FP32 = 2 };
+enum { OR_PATH_INT8 = 0, OR_PATH_BF16 = 1 };
+enum { OR_OK = 0, OR_ERR_ARG = 1, OR_ERR_SHAPE = 2 };
+
+/* ---------------------------------------------------------------- decoding */
+
+static float bits_to_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t f32_to_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/* bf16 -> fp32 is exact: the bf16 word is the top half of the fp32 word. */
+float oracle_bf16_to_f32(uint16_t b) { return bits_to_f32((uint32_t)b << 16); }
+
+/* IEEE binary16 -> double, exact, written out from the format definition. */
+double oracle_fp16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int exp = (h >> 10) & 0x1F;
+    int man = h & 0x3FF;
+    double v;
+    if (exp == 0)
+        v = ldexp((double)man, -24); /* subnormal: man * 2^-14 * 2^-10 */
+    else if (exp == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man + 1024), exp - 25); /* 1.man * 2^(exp-15) */
+    return sign ? -v : v;
+}
+
+/*
+ * double -> bf16, round to nearest, ties to even, in ONE rounding (no pass
+ * through fp32, which could round twice).  bf16 carries 8 significant bits
+ * and the fp32 exponent range, so a value in [2^(e-1), 2^e) is a multiple of
+ * 2^(e-8); below 2^-126 the spacing is fixed at 2^-133 (subnormals).
+ */
+uint16_t oracle_f64_to_bf16(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int e;
+    frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+    int qexp = e - 8;
+    if (qexp < -133) qexp = -133;
+    double n = nearbyint(ldexp(a, -qexp)); /* exact scaling; default mode is nearest-even */
+    double r = ldexp(n, qexp);
+    if (r >= 0x1p128) return sign | 0x7F80; /* overflow */
+    return sign | (uint16_t)(f32_to_bits((float)r) >> 16); /* r is a bf16 value: exact */
+}
+
+/* ---------------------------------------------------------------- quantize */
+
+/*
+ * Block-absmax INT8 quantization of a row-major bf16 matrix x[rows, cols]:
+ * for each 128x128 block, a = max |x| (exact), s = fl32(a / 127),
+ * q = clamp(rint(fl32(x / s)), -127, 127), or s = 0 and q = 0 when a = 0.
+ * q is row-major [rows, cols]; s is row-major [rows/128, cols/128].
+ */
+int oracle_quantize_block(const uint16_t *x, int64_t rows, int64_t cols, int8_t *q, float *s) {
+    if (!x || !q || !s || rows <= 0 || cols <= 0) return OR_ERR_ARG;
+    if (rows % ORACLE_BLOCK || cols % ORACLE_BLOCK) return OR_ERR_SHAPE;
+    const int64_t rb = rows / ORACLE_BLOCK, cb = cols / ORACLE_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t blk = 0; blk < rb * cb; ++blk) {
+        const int64_t bi = blk / cb, bj = blk % cb;
+        const int64_t r0 = bi * ORACLE_BLOCK, c0 = bj * ORACLE_BLOCK;
+        float a = 0.0f;
+        for (int64_t r = r0; r < r0 + ORACLE_BLOCK; ++r)
+            for (int64_t c = c0; c < c0 + ORACLE_BLOCK; ++c) {
+                float v = fabsf(oracle_bf16_to_f32(x[r * cols + c]));
+                if (v > a) a = v;
+            }
+        const float sc = a / 127.0f;
+        s[bi * cb + bj] = sc;
+        for (int64_t r = r0; r < r0 + ORACLE_BLOCK; ++r)
+            for (int64_t c = c0; c < c0 + ORACLE_BLOCK; ++c) {
+                int8_t out = 0;
+                if (a != 0.0f) {
+                    float t = rintf(oracle_bf16_to_f32(x[r * cols + c]) / sc);
+                    if (t > 127.0f) t = 127.0f;
+                    if (t < -127.0f) t = -127.0f;
+                    out = (int8_t)t;
+                }
+                q[r * cols + c] = out;
+            }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------- per-K-block partials */
+
+/*
+ * P[m, n, kb] = sum over the 128 k of K-block kb of qx[m, k] * qw[n, k], in
+ * int32 (|P| <= 128 * 127^2 = 2,064,512, no overflow).  Window: rows
+ * [m0, m0+mt) of qx and rows [n0, n0+nt) of qw; out is [mt, nt, K/128].
+ */
+int oracle_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N, int64_t K,
+                           int64_t m0, int64_t mt, int64_t n0, int64_t nt, int32_t *out) {
+    if (!qx || !qw || !out || M <= 0 || N <= 0 || K <= 0) return OR_ERR_ARG;
+    if (K % ORACLE_BLOCK) return OR_ERR_SHAPE;
+    if (m0 < 0 || mt <= 0 || m0 + mt > M || n0 < 0 || nt <= 0 || n0 + nt > N) return OR_ERR_ARG;
+    const int64_t kbs = K / ORACLE_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < mt; ++i)
+        for (int64_t j = 0; j < nt; ++j)
+            for (int64_t kb = 0; kb < kbs; ++kb) {
+                int32_t acc = 0;
+                for (int64_t k = kb * ORACLE_BLOCK; k < (kb + 1) * ORACLE_BLOCK; ++k)
+                    acc += (int32_t)qx[(m0 + i) * K + k] * (int32_t)qw[(n0 + j) * K + k];
+                out[(i * nt + j) * kbs + kb] = acc;
+            }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------ dequantized output */
+
+/*
+ * Y[m, n] = bf16( sum_kb P[m, n, kb] * sx[m/128, kb] * sw[n/128, kb]
+ *                 (+ bias[n]) ), accumulated in fp64 and rounded once.
+ * Only the listed rows are computed (rows == NULL: all M rows, in order);
+ * y is [nrows, N].  If y_f64 is not NULL it receives the unrounded fp64 sum.
+ */
+int oracle_linear_int8_rows(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                            const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                            const int64_t *rows, int64_t nrows, uint16_t *y, double *y_f64) {
+    if (!qx || !sx || !qw || !sw || (!y && !y_f64) || M <= 0 || N <= 0 || K <= 0) return OR_ERR_ARG;
+    if (M % ORACLE_BLOCK || N % ORACLE_BLOCK || K % ORACLE_BLOCK) return OR_ERR_SHAPE;
+    if (!rows) nrows = M;
+    if (nrows <= 0) return OR_ERR_ARG;
+    const int64_t kbs = K / ORACLE_BLOCK;
+    for (int64_t t = 0; t < nrows; ++t)
+        if (rows && (rows[t] < 0 || rows[t] >= M)) return OR_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t m = rows ? rows[t] : t;
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < kbs; ++kb) {
+                int32_t p = 0;
+                for (int64_t k = kb * ORACLE_BLOCK; k < (kb + 1) * ORACLE_BLOCK; ++k)
+                    p += (int32_t)qx[m * K + k] * (int32_t)qw[n * K + k];
+                acc += (double)p * (double)sx[(m / ORACLE_BLOCK) * kbs + kb] *
+                       (double)sw[(n / ORACLE_BLOCK) * kbs + kb];
+            }
+            if (bias) acc += (double)oracle_bf16_to_f32(bias[n]);
+            if (y) y[t * N + n] = oracle_f64_to_bf16(acc);
+            if (y_f64) y_f64[t * N + n] = acc;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------ bf16 fallback */
+
+static double load_as_bf16(const void *x, int dtype, int64_t idx) {
+    switch (dtype) {
+    case OR_DTYPE_BF16:
+        return (double)oracle_bf16_to_f32(((const uint16_t *)x)[idx]);
+    case OR_DTYPE_FP16:
+        return (double)oracle_bf16_to_f32(oracle_f64_to_bf16(oracle_fp16_to_f64(((const uint16_t *)x)[idx])));
+    default:
+        return (double)oracle_bf16_to_f32(oracle_f64_to_bf16((double)((const float *)x)[idx]));
+    }
+}
+
+/*
+ * Native bf16 linear on the retained bf16 weight, any M, N, K >= 1:
+ * Y[m, n] = bf16( sum_k bf16(x[m, k]) * w[n, k] (+ bias[n]) ), fp64 sum.
+ */
+int oracle_linear_bf16_rows(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
+                            int64_t M, int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                            uint16_t *y) {
+    if (!x || !w || !y || M <= 0 || N <= 0 || K <= 0) return OR_ERR_ARG;
+    if (x_dtype < OR_DTYPE_BF16 || x_dtype > OR_DTYPE_FP32) return OR_ERR_ARG;
+    if (!rows) nrows = M;
+    if (nrows <= 0) return OR_ERR_ARG;
+    for (int64_t t = 0; t < nrows; ++t)
+        if (rows && (rows[t] < 0 || rows[t] >= M)) return OR_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t m = rows ? rows[t] : t;
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += load_as_bf16(x, x_dtype, m * K + k) * (double)oracle_bf16_to_f32(w[n * K + k]);
+            if (bias) acc += (double)oracle_bf16_to_f32(bias[n]);
+            y[t * N + n] = oracle_f64_to_bf16(acc);
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------- guard */
+
+/*
+ * INT8 path iff the input is bf16, M, K and N are multiples of 128 and a
+ * quantized weight exists; every other valid call takes the bf16 fallback.
+ * Returns -1 for invalid arguments (non-positive sizes, unknown dtype).
+ */
+int oracle_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight) {
+    if (M <= 0 || K <= 0 || N <= 0) return -1;
+    if (x_dtype < OR_DTYPE_BF16 || x_dtype > OR_DTYPE_FP32) return -1;
+    if (x_dtype == OR_DTYPE_BF16 && M % ORACLE_BLOCK == 0 && K % ORACLE_BLOCK == 0 &&
+        N % ORACLE_BLOCK == 0 && has_qweight)
+        return OR_PATH_INT8;
+    return OR_PATH_BF16;
+}
+
+/* ------------------------------------------------- test-harness producer */
+
+/*
+ * Exact-erf GELU in fp64, rounded once to bf16: the producer between the two
+ * linears of the MLP-pair workload (not part of the linear layer itself).
+ */
+int oracle_gelu_bf16(const uint16_t *x, int64_t n, uint16_t *y) {
+    if (!x || !y || n < 0) return OR_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double v = (double)oracle_bf16_to_f32(x[i]);
+        y[i] = oracle_f64_to_bf16(0.5 * v * (1.0 + erf(v / sqrt(2.0))));
+    }
+    return OR_OK;
+}
+
+/* Threads an OpenMP region of this library will use. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
