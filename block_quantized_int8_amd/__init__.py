@@ -1,0 +1,187 @@
+"""Guarded W8A8 block-quantized INT8 linear for AMD MI355X (gfx950).
+
+Thin torch-facing wrappers over the C ABI of libw8a8.so (include/w8a8.h).
+torch provides device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  Function names follow the
+C entry points:
+
+* ``quantize_weight(w)``   -> (qw int8 [N,K], sw fp32 [N/128, K/128])  (static)
+* ``quantize_act(x)``      -> (qx int8 [M,K], sx fp32 [M/128, K/128])  (dynamic)
+* ``gemm_blockscale(qx, sx, qw, sw, bias)`` -> Y bf16 [M, N]
+* ``linear(x, w, qw, sw, bias)``            -> (Y bf16 [..., N], path)  guarded
+* ``route(dtype, M, K, N, has_qweight)``    -> path (host only)
+* ``debug_kblock_partials(qx, qw, m0, mt, n0, nt)`` -> int32 [mt, nt, K/128]
+* ``W8A8Linear``: a linear layer that quantizes its weight once at
+  construction and keeps the bf16 copy for the fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP16, DTYPE_FP32, EXPORTS, PATH_BF16, PATH_INT8,
+                   W8A8Error, check, lib)
+
+__all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "route",
+           "workspace_bytes", "debug_kblock_partials", "W8A8Linear", "W8A8Error", "lib",
+           "PATH_INT8", "PATH_BF16", "DTYPE_BF16", "DTYPE_FP16", "DTYPE_FP32", "BLOCK", "EXPORTS"]
+
+_DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32: DTYPE_FP32}
+
+
+def _need_cuda(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def route(dtype, M: int, K: int, N: int, has_qweight: bool) -> int:
+    """The guard (host only). ``dtype`` is a torch dtype or a DTYPE_* code."""
+    code = _DTYPES.get(dtype, dtype) if isinstance(dtype, torch.dtype) else dtype
+    if isinstance(dtype, torch.dtype) and dtype not in _DTYPES:
+        code = 99
+    return lib().w8a8_route(int(code), int(M), int(K), int(N), int(bool(has_qweight)))
+
+
+def workspace_bytes(M: int, K: int) -> int:
+    return int(lib().w8a8_linear_workspace_bytes(int(M), int(K)))
+
+
+def _quantize(fn, name, x):
+    _need_cuda(name, x, torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    s = torch.empty((max(R // BLOCK, 1), max(C // BLOCK, 1)), dtype=torch.float32, device=x.device)
+    check(fn.__name__, fn(_ptr(x), R, C, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def quantize_weight(w: torch.Tensor):
+    """Static 128x128 block INT8 quantization of a bf16 weight [N, K]."""
+    return _quantize(lib().w8a8_quantize_weight, "w", w)
+
+
+def quantize_act(x: torch.Tensor):
+    """Dynamic 128x128 block INT8 quantization of bf16 activations [M, K]."""
+    return _quantize(lib().w8a8_quantize_act, "x", x)
+
+
+def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):
+    """INT8 GEMM with per-K-block dequantization -> bf16 [M, N]."""
+    _need_cuda("qx", qx, torch.int8)
+    _need_cuda("qw", qw, torch.int8)
+    _need_cuda("sx", sx, torch.float32)
+    _need_cuda("sw", sw, torch.float32)
+    M, K = qx.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("qx and qw disagree on K")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
+    _need_cuda("out", out, torch.bfloat16)
+    check("w8a8_gemm_blockscale",
+          lib().w8a8_gemm_blockscale(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(bias), M, N, K,
+                                     _ptr(out), _stream(qx.device)))
+    return out
+
+
+def linear(x, w, qw=None, sw=None, bias=None, out=None, workspace=None):
+    """Guarded W8A8 linear: Y = x @ w.T (+ bias) in bf16; returns (Y, path).
+
+    x may be bf16, fp16 or fp32 with any leading dims (flattened to M rows).
+    The INT8 path needs bf16 x, M, K, N multiples of 128 and (qw, sw);
+    everything else runs the bf16 fallback on ``w``.
+    """
+    if not isinstance(x, torch.Tensor) or x.dtype not in _DTYPES:
+        raise ValueError("x must be a bf16, fp16 or fp32 tensor")
+    _need_cuda("w", w, torch.bfloat16)
+    N, K = w.shape
+    if x.shape[-1] != K:
+        raise ValueError("x and w disagree on K")
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, K)
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    _need_cuda("x", x2)
+    M = x2.shape[0]
+    if (qw is None) != (sw is None):
+        raise ValueError("qw and sw go together")
+    if qw is not None:
+        _need_cuda("qw", qw, torch.int8)
+        _need_cuda("sw", sw, torch.float32)
+    if bias is not None:
+        _need_cuda("bias", bias, torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need_cuda("out", out, torch.bfloat16)
+    need = workspace_bytes(M, K) if qw is not None else 0
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    path = ctypes.c_int(-1)
+    check("w8a8_linear",
+          lib().w8a8_linear(_ptr(x2), _DTYPES[x.dtype], M, K, N, _ptr(w), _ptr(qw), _ptr(sw),
+                            _ptr(bias), _ptr(out), _ptr(workspace) if need else None,
+                            need, _stream(x.device), ctypes.byref(path)))
+    return out.reshape(*lead, N), path.value
+
+
+def debug_kblock_partials(qx, qw, m0: int, mt: int, n0: int, nt: int):
+    """Exact int32 per-K-block partial sums of a 128-aligned output window."""
+    _need_cuda("qx", qx, torch.int8)
+    _need_cuda("qw", qw, torch.int8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    out = torch.empty((mt, nt, K // BLOCK), dtype=torch.int32, device=qx.device)
+    check("w8a8_debug_kblock_partials",
+          lib().w8a8_debug_kblock_partials(_ptr(qx), _ptr(qw), M, N, K, m0, mt, n0, nt, _ptr(out),
+                                           _stream(qx.device)))
+    return out
+
+
+class W8A8Linear(torch.nn.Module):
+    """Linear layer on the guarded W8A8 path.
+
+    The bf16 weight [N, K] is kept (the fallback needs it) and, when N and K
+    are multiples of 128, quantized once here.  ``forward`` quantizes the
+    activations on every call (or falls back) and returns bf16.
+    """
+
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None):
+        super().__init__()
+        _need_cuda("weight", weight, torch.bfloat16)
+        self.weight = weight
+        self.bias = bias
+        N, K = weight.shape
+        if N % BLOCK == 0 and K % BLOCK == 0:
+            self.qweight, self.wscale = quantize_weight(weight)
+        else:
+            self.qweight, self.wscale = None, None
+        self._workspace = None
+        self.last_path = None
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        K = self.weight.shape[1]
+        M = x.numel() // K if K else 0
+        need = workspace_bytes(M, K) if self.qweight is not None else 0
+        if need and (self._workspace is None or self._workspace.numel() < need
+                     or self._workspace.device != x.device):
+            self._workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        y, self.last_path = linear(x, self.weight, self.qweight, self.wscale, self.bias,
+                                   workspace=self._workspace)
+        return y

@@ -1,0 +1,205 @@
+// bf16 fallback linear on gfx950 matrix cores: the guard's "otherwise" path.
+//
+//   Y[m, n] = bf16( sum_k bf16(x[m, k]) * w[n, k] (+ bias[n]) ), fp32 sums,
+//
+// for any M, N, K >= 1, with the retained bf16 weight copy (TurboT2VA paper,
+// architecture-aware inference stack, guard paragraph: unsupported dtypes or
+// shapes run a native BF16 linear on the kept BF16 weights).  fp16 and fp32
+// inputs are rounded to bf16 (nearest even) as they are loaded.
+//
+// One workgroup (4 wavefronts) per 128x128 output tile, 64-deep K steps
+// staged through double-buffered LDS (128-byte rows, XOR-swizzled 16-byte
+// chunks, as in the INT8 kernel).  v_mfma_f32_32x32x16_bf16 accumulates in
+// fp32 across all of K.  Out-of-range rows and K positions are loaded as
+// zeros; stores are predicated per element.  kVec selects 16-byte loads
+// (bf16 input, K % 8 == 0, 16-byte aligned operands); otherwise elements are
+// loaded one by one (per operand: the weight's loads are vectorized
+// whenever K % 8 == 0 and it is 16-byte aligned).
+#include "w8a8_internal.h"
+
+namespace w8a8 {
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kStepK = 64;   // bf16 elements per K step (128 bytes per row)
+constexpr int kThreads = 256;
+constexpr int kLdsTile = kTile * kStepK * 2;  // bytes per operand per stage
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
+}
+
+template <int kDtype>
+__device__ __forceinline__ uint16_t load_as_bf16(const void *p, int64_t idx) {
+    if constexpr (kDtype == 0) {
+        return static_cast<const uint16_t *>(p)[idx];
+    } else if constexpr (kDtype == 1) {
+        return f32_to_bf16_bits((float)static_cast<const _Float16 *>(p)[idx]);
+    } else {
+        return f32_to_bf16_bits(static_cast<const float *>(p)[idx]);
+    }
+}
+
+// One 16-byte chunk (8 consecutive k) of row `row` starting at column k0,
+// zero outside [0, rows) x [0, K).
+template <int kDtype, bool kVec>
+__device__ __forceinline__ u32x4 load_chunk(const void *base, int64_t row, int64_t rows, int64_t k0,
+                                            int64_t K) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row >= rows || k0 >= K) return v;
+    if constexpr (kVec) {
+        return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + row * K + k0);
+    } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = (k0 + i < K) ? load_as_bf16<kDtype>(base, row * K + k0 + i) : 0;
+        v.x = e[0] | ((uint32_t)e[1] << 16);
+        v.y = e[2] | ((uint32_t)e[3] << 16);
+        v.z = e[4] | ((uint32_t)e[5] << 16);
+        v.w = e[6] | ((uint32_t)e[7] << 16);
+        return v;
+    }
+}
+
+template <int kDtype, bool kVecX, bool kVecW>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const void *__restrict__ x,
+                                                             const uint16_t *__restrict__ w,
+                                                             const uint16_t *__restrict__ bias,
+                                                             uint16_t *__restrict__ y, int64_t M,
+                                                             int64_t N, int64_t K, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kLdsTile];
+    const int t = blockIdx.x;
+    const int mb = t / tiles_n, nb = t - mb * tiles_n;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    int crow[4], cch[4], l_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + i * kThreads;
+        crow[i] = c >> 3;
+        cch[i] = c & 7;
+        l_off[i] = swz(crow[i], cch[i]);
+    }
+    const int64_t m_base = (int64_t)mb * kTile, n_base = (int64_t)nb * kTile;
+
+    u32x4 rx[4], rw[4];
+    auto load_tiles = [&](int64_t ks) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t k0 = ks * kStepK + cch[i] * 8;
+            rx[i] = load_chunk<kDtype, kVecX>(x, m_base + crow[i], M, k0, K);
+            rw[i] = load_chunk<0, kVecW>(w, n_base + crow[i], N, k0, K);
+        }
+    };
+    auto store_tiles = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4 *>(&lds[buf][0][l_off[i]]) = rx[i];
+            *reinterpret_cast<u32x4 *>(&lds[buf][1][l_off[i]]) = rw[i];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t KS = (K + kStepK - 1) / kStepK;
+    load_tiles(0);
+    store_tiles(0);
+    __syncthreads();
+
+    const int frag_row = lane & 31, frag_half = lane >> 5;
+    for (int64_t ks = 0; ks < KS; ++ks) {
+        const int buf = (int)(ks & 1);
+        if (ks + 1 < KS) load_tiles(ks + 1);
+        bf16x8 fx[2][4], fw[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int row = wm * 64 + j * 32 + frag_row;
+                fx[j][kk] = *reinterpret_cast<const bf16x8 *>(&lds[buf][0][swz(row, kk * 2 + frag_half)]);
+            }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int row = wn * 64 + i * 32 + frag_row;
+                fw[i][kk] = *reinterpret_cast<const bf16x8 *>(&lds[buf][1][swz(row, kk * 2 + frag_half)]);
+            }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i][kk], fx[j][kk], acc[i][j], 0, 0, 0);
+        if (ks + 1 < KS) store_tiles(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t m = m_base + wm * 64 + j * 32 + frag_row;
+            if (m >= M) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n_base + wn * 64 + i * 32 + q * 8 + frag_half * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (n + e < N) {
+                        float v = acc[i][j][q * 4 + e];
+                        if (bias) v += __uint_as_float((uint32_t)bias[n + e] << 16);
+                        y[m * N + n + e] = f32_to_bf16_bits(v);
+                    }
+                }
+            }
+        }
+}
+
+template <int kDtype, bool kVecX, bool kVecW>
+hipError_t launch_typed(const void *x, const uint16_t *w, const uint16_t *bias, int64_t M, int64_t N,
+                        int64_t K, uint16_t *y, hipStream_t stream) {
+    const int64_t tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
+    if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemm_bf16_kernel<kDtype, kVecX, kVecW><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+        x, w, bias, y, M, N, K, (int)tn);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
+                            int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+    const bool vec_w = (K % 8 == 0) && ((uintptr_t)w % 16 == 0);
+    const bool vec_x = (x_dtype == 0) && vec_w && ((uintptr_t)x % 16 == 0);
+    if (vec_x) return launch_typed<0, true, true>(x, w, bias, M, N, K, y, stream);
+    switch (x_dtype) {
+    case 0:
+        return vec_w ? launch_typed<0, false, true>(x, w, bias, M, N, K, y, stream)
+                     : launch_typed<0, false, false>(x, w, bias, M, N, K, y, stream);
+    case 1:
+        return vec_w ? launch_typed<1, false, true>(x, w, bias, M, N, K, y, stream)
+                     : launch_typed<1, false, false>(x, w, bias, M, N, K, y, stream);
+    default:
+        return vec_w ? launch_typed<2, false, true>(x, w, bias, M, N, K, y, stream)
+                     : launch_typed<2, false, false>(x, w, bias, M, N, K, y, stream);
+    }
+}
+
+}  // namespace w8a8

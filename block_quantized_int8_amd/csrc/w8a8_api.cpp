@@ -1,0 +1,155 @@
+// C ABI of libw8a8: argument checks, the guard (router) and kernel launches.
+// Every entry point is declared and documented in include/w8a8.h.
+#include "w8a8.h"
+
+#include <hip/hip_runtime.h>
+
+#include "w8a8_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return W8A8_OK;
+    g_last_hip_error = (int)e;
+    return W8A8_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// True iff HIP knows p as device (or managed) memory.  Rejecting anything
+// else up front keeps a host pointer from ever reaching a kernel.
+bool is_device_ptr(const void *p) {
+    if (!p) return false;
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error this query may leave
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+bool valid_dtype(int d) { return d == W8A8_DTYPE_BF16 || d == W8A8_DTYPE_FP16 || d == W8A8_DTYPE_FP32; }
+
+bool mult128(int64_t v) { return v > 0 && v % W8A8_BLOCK == 0; }
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int quantize_strict(const void *x, int64_t R, int64_t C, int8_t *q, float *s, hipStream_t stream) {
+    if (!x || !q || !s || R <= 0 || C <= 0) return W8A8_ERR_INVALID_ARG;
+    if (!mult128(R) || !mult128(C)) return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x) || !is_device_ptr(q) || !is_device_ptr(s)) return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_quantize_block(static_cast<const uint16_t *>(x), R, C, q, s, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int w8a8_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight) {
+    if (M <= 0 || K <= 0 || N <= 0 || !valid_dtype(x_dtype)) return -1;
+    if (x_dtype == W8A8_DTYPE_BF16 && M % W8A8_BLOCK == 0 && K % W8A8_BLOCK == 0 &&
+        N % W8A8_BLOCK == 0 && has_qweight)
+        return W8A8_PATH_INT8;
+    return W8A8_PATH_BF16;
+}
+
+int w8a8_quantize_weight(const void *w_bf16, int64_t N, int64_t K, int8_t *qw, float *sw,
+                         hipStream_t stream) {
+    return quantize_strict(w_bf16, N, K, qw, sw, stream);
+}
+
+int w8a8_quantize_act(const void *x_bf16, int64_t M, int64_t K, int8_t *qx, float *sx,
+                      hipStream_t stream) {
+    return quantize_strict(x_bf16, M, K, qx, sx, stream);
+}
+
+int w8a8_gemm_blockscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                         const void *bias_bf16, int64_t M, int64_t N, int64_t K, void *y_bf16,
+                         hipStream_t stream) {
+    if (!qx || !sx || !qw || !sw || !y_bf16 || M <= 0 || N <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
+    if (!mult128(M) || !mult128(N) || !mult128(K)) return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(y_bf16, 16) || !aligned(sx, 4) ||
+        !aligned(sw, 4) || !aligned(bias_bf16, 8))
+        return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(qx) || !is_device_ptr(sx) || !is_device_ptr(qw) || !is_device_ptr(sw) ||
+        !is_device_ptr(y_bf16) || (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_gemm_i8_blockscale(qx, sx, qw, sw,
+                                                      static_cast<const uint16_t *>(bias_bf16), M, N,
+                                                      K, static_cast<uint16_t *>(y_bf16), stream));
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
+    if (!mult128(M) || !mult128(K)) return 0;
+    const size_t q = round256((size_t)M * (size_t)K);
+    const size_t s = round256((size_t)(M / W8A8_BLOCK) * (size_t)(K / W8A8_BLOCK) * sizeof(float));
+    return q + s;
+}
+
+int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
+                const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
+                void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out) {
+    if (!x || !w_bf16 || !y_bf16 || M <= 0 || K <= 0 || N <= 0 || !valid_dtype(x_dtype))
+        return W8A8_ERR_INVALID_ARG;
+    if ((qw == nullptr) != (sw == nullptr)) return W8A8_ERR_INVALID_ARG;
+    if (!is_device_ptr(x) || !is_device_ptr(w_bf16) || !is_device_ptr(y_bf16) ||
+        (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+
+    int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
+    if (path == W8A8_PATH_INT8) {
+        const size_t need = w8a8_linear_workspace_bytes(M, K);
+        if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
+        if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace))
+            return W8A8_ERR_INVALID_ARG;
+        // the INT8 kernels use 16-byte loads/stores; otherwise fall back
+        if (!aligned(x, 16) || !aligned(y_bf16, 16) || !aligned(qw, 16) || !aligned(workspace, 16) ||
+            !aligned(sw, 4) || !aligned(bias_bf16, 8))
+            path = W8A8_PATH_BF16;
+    }
+    if (path_out) *path_out = path;
+
+    if (path == W8A8_PATH_INT8) {
+        int8_t *qx = static_cast<int8_t *>(workspace);
+        float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) + round256((size_t)M * (size_t)K));
+        hipError_t e = w8a8::launch_quantize_block(static_cast<const uint16_t *>(x), M, K, qx, sx, stream);
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(w8a8::launch_gemm_i8_blockscale(qx, sx, qw, sw,
+                                                          static_cast<const uint16_t *>(bias_bf16), M,
+                                                          N, K, static_cast<uint16_t *>(y_bf16), stream));
+    }
+    return hip_status(w8a8::launch_gemm_bf16(x, x_dtype, static_cast<const uint16_t *>(w_bf16),
+                                             static_cast<const uint16_t *>(bias_bf16), M, N, K,
+                                             static_cast<uint16_t *>(y_bf16), stream));
+}
+
+int w8a8_debug_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N, int64_t K,
+                               int64_t m0, int64_t mt, int64_t n0, int64_t nt, int32_t *partials,
+                               hipStream_t stream) {
+    if (!qx || !qw || !partials || M <= 0 || N <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
+    if (m0 < 0 || n0 < 0 || mt <= 0 || nt <= 0 || m0 + mt > M || n0 + nt > N) return W8A8_ERR_INVALID_ARG;
+    if (!mult128(M) || !mult128(N) || !mult128(K) || m0 % W8A8_BLOCK || n0 % W8A8_BLOCK ||
+        mt % W8A8_BLOCK || nt % W8A8_BLOCK)
+        return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(partials, 4)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(qx) || !is_device_ptr(qw) || !is_device_ptr(partials)) return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_kblock_partials(qx, qw, M, N, K, m0, mt, n0, nt, partials, stream));
+}
+
+const char *w8a8_status_string(int status) {
+    switch (status) {
+    case W8A8_OK: return "W8A8_OK";
+    case W8A8_ERR_INVALID_ARG: return "W8A8_ERR_INVALID_ARG";
+    case W8A8_ERR_UNSUPPORTED: return "W8A8_ERR_UNSUPPORTED";
+    case W8A8_ERR_HIP: return "W8A8_ERR_HIP";
+    default: return "W8A8_UNKNOWN_STATUS";
+    }
+}
+
+int w8a8_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+/*
+ * w8a8.h -- guarded W8A8 block-quantized linear layer for AMD MI355X (gfx950).
+ *
+ * The operation (Y = X * W^T for a linear layer, X[M,K] activations, W[N,K]
+ * output-channel weight rows) is the guarded INT8 linear of the TurboT2VA
+ * inference stack, in the 128x128 block form:
+ *
+ *   - weights and activations are quantized to INT8 per 128x128 block
+ *     (TurboDiffusion news article, bjdmk.com.cn: quantization section and
+ *     inference list -- linear weights at 128x128 block granularity,
+ *     activations at the same granularity during inference, INT8 GEMM);
+ *   - each block's scale is its max-abs value divided by 127, weights are
+ *     quantized once ("static"), activations on every call ("dynamic"),
+ *     products accumulate in INT32 and scales/bias are applied in the
+ *     epilogue (TurboT2VA paper, arXiv 2608.24674, architecture-aware
+ *     inference stack, W8A8 linear paragraph -- there per row/channel; here
+ *     per block, so the INT32 sum is exact within each 128-deep K-block and
+ *     the block scales are applied once per K-block);
+ *   - the guard: the INT8 path needs a BF16 input and M, K, N divisible by
+ *     128; otherwise a BF16 linear runs on the retained BF16 weight copy
+ *     (TurboT2VA paper, same section, guard paragraph; pchao.org summary,
+ *     method overview and caveats).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE memory (HIP), row-major and contiguous.
+ *     bf16 and fp16 tensors are arrays of 16-bit words.  A host pointer, or
+ *     any pointer HIP does not know as device-accessible, is rejected with
+ *     W8A8_ERR_INVALID_ARG before anything is enqueued.
+ *   - Quantized tensors: q int8 [R, C] with the same layout as the source,
+ *     scales fp32 [R/128, C/128] row-major (block (i, j) covers rows
+ *     128i..128i+127 and columns 128j..128j+127).
+ *   - Quantization: a = max |v| over the block (exact), s = fl32(a / 127),
+ *     q = rint(fl32(v / s)) (ties to even, correctly rounded division),
+ *     clamped to [-127, 127]; an all-zero block has s = 0 and q = 0.
+ *     Inputs must be finite.
+ *   - Ownership: the caller allocates every buffer (including the
+ *     workspace) and keeps it alive until the enqueued work completes.  The
+ *     library never allocates, frees, copies to or from the host, or
+ *     synchronizes; all work is enqueued on `stream` (0 = null stream).
+ *   - Errors: integer status, nothing thrown.  On an error detected before a
+ *     launch nothing is enqueued.  W8A8_ERR_HIP means a HIP call failed; the
+ *     HIP error code is kept per thread (w8a8_last_hip_error).
+ *   - The library is stateless apart from that per-thread slot: calls are
+ *     reentrant; calls on different streams may run concurrently.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { W8A8_OK = 0, W8A8_ERR_INVALID_ARG = 1, W8A8_ERR_UNSUPPORTED = 2, W8A8_ERR_HIP = 3 };
+enum { W8A8_DTYPE_BF16 = 0, W8A8_DTYPE_FP16 = 1, W8A8_DTYPE_FP32 = 2 };
+enum { W8A8_PATH_INT8 = 0, W8A8_PATH_BF16 = 1 };
+#define W8A8_BLOCK 128
+
+/*
+ * Static weight quantization (done once, at load): w_bf16 [N, K] ->
+ * qw int8 [N, K] and sw fp32 [N/128, K/128].
+ * Strict: N or K not a multiple of 128, or w_bf16/qw not 16-byte aligned ->
+ * W8A8_ERR_UNSUPPORTED.  Null pointers or N, K <= 0 -> W8A8_ERR_INVALID_ARG.
+ */
+int w8a8_quantize_weight(const void *w_bf16, int64_t N, int64_t K, int8_t *qw, float *sw,
+                         hipStream_t stream);
+
+/*
+ * Dynamic activation quantization (every call): x_bf16 [M, K] ->
+ * qx int8 [M, K] and sx fp32 [M/128, K/128].  Same rule and errors as
+ * w8a8_quantize_weight.
+ */
+int w8a8_quantize_act(const void *x_bf16, int64_t M, int64_t K, int8_t *qx, float *sx,
+                      hipStream_t stream);
+
+/*
+ * INT8 GEMM on already-quantized operands with per-K-block dequantization:
+ *   Y[m, n] = bf16( sum_kb  P[m, n, kb] * sx[m/128, kb] * sw[n/128, kb]
+ *                   (+ bias[n]) ),
+ *   P[m, n, kb] = exact int32 sum over the 128 k of K-block kb of
+ *                 qx[m, k] * qw[n, k].
+ * The sum over K-blocks is carried in fp32; bias (bf16 [N], nullable) is
+ * added in fp32; Y is bf16 [M, N], rounded to nearest even.
+ * Strict: M, N, K multiples of 128 and qx, qw, y 16-byte aligned, else
+ * W8A8_ERR_UNSUPPORTED.
+ */
+int w8a8_gemm_blockscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                         const void *bias_bf16, int64_t M, int64_t N, int64_t K, void *y_bf16,
+                         hipStream_t stream);
+
+/*
+ * Bytes of workspace w8a8_linear needs for the INT8 path: qx [M, K] plus sx
+ * [M/128, K/128], each 256-byte aligned inside the workspace.  0 when M or K
+ * is not a multiple of 128 (such calls always take the fallback).
+ */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * Guarded linear: Y[M, N] (bf16) = X[M, K] * W[N, K]^T (+ bias).
+ *   x        : [M, K], dtype x_dtype (W8A8_DTYPE_*), M = flattened leading dims
+ *   w_bf16   : retained bf16 weight [N, K] (required: the fallback uses it)
+ *   qw, sw   : w8a8_quantize_weight outputs for w_bf16 (both null -> no
+ *              INT8 path; exactly one null -> W8A8_ERR_INVALID_ARG)
+ *   bias_bf16: [N] or null
+ *   y_bf16   : [M, N] output
+ *   workspace: >= w8a8_linear_workspace_bytes(M, K) bytes when the INT8
+ *              path is taken (may be null/0 otherwise)
+ *   path_out : if not null, receives the W8A8_PATH_* taken
+ * INT8 path iff w8a8_route(...) == W8A8_PATH_INT8 and x, y, qw and the
+ * workspace are 16-byte aligned: then the activation is quantized into the
+ * workspace and w8a8_gemm_blockscale's computation runs.  Otherwise the bf16
+ * fallback runs: Y = bf16( sum_k bf16(x[m,k]) * w[n,k] (+ bias[n]) ) with
+ * fp32 accumulation; fp16/fp32 x is rounded to bf16 (nearest even) on load.
+ * Never fails on dtype or shape: returns W8A8_ERR_INVALID_ARG only for null
+ * required pointers, sizes <= 0, an unknown dtype, a host pointer, or a
+ * workspace smaller than needed by the INT8 path.
+ */
+int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
+                const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
+                void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out);
+
+/*
+ * The guard alone (host only, pure, touches no device): W8A8_PATH_INT8 iff
+ * x_dtype is bf16, M, K and N are multiples of 128 and has_qweight != 0;
+ * W8A8_PATH_BF16 for every other valid call; -1 for sizes <= 0 or an
+ * unknown dtype.  w8a8_linear additionally sends misaligned pointers to the
+ * fallback.
+ */
+int w8a8_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight);
+
+/*
+ * Test hook: the INT8 GEMM's main loop with an epilogue that stores the
+ * exact int32 per-K-block partials instead of dequantizing them.
+ * Window rows [m0, m0+mt) of qx and [n0, n0+nt) of qw; m0, mt, n0, nt
+ * multiples of 128 inside the matrices; partials int32 [mt, nt, K/128].
+ * Strict shape/alignment rules as w8a8_gemm_blockscale.
+ */
+int w8a8_debug_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N, int64_t K,
+                               int64_t m0, int64_t mt, int64_t n0, int64_t nt, int32_t *partials,
+                               hipStream_t stream);
+
+/* Static, human-readable name of a W8A8_* status code. */
+const char *w8a8_status_string(int status);
+
+/* hipError_t of the last W8A8_ERR_HIP returned on this thread (0 if none). */
+int w8a8_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,77 @@
+"""GPU INT8 GEMM vs the oracle: per-K-block int32 partials bit-exact,
+dequantized bf16 output within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_int8_amd as w8a8
+import oracle
+from block_quantized_int8_amd.workloads import c1, random_bf16
+from parity import assert_bf16_close, bf16_bits, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def test_partials_c1_full():
+    d = c1()
+    qx, sx = oracle.quantize_block(d["x"])
+    qw, sw = oracle.quantize_block(d["w"])
+    p = w8a8.debug_kblock_partials(_dev(qx), _dev(qw), 0, 256, 0, 256)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), oracle.kblock_partials(qx, qw))
+
+
+@pytest.mark.parametrize("M,N,K,win", [(384, 256, 640, (128, 256, 0, 256)),
+                                       (256, 512, 384, (0, 256, 384, 128)),
+                                       (128, 128, 128, (0, 128, 0, 128))])
+def test_partials_windows(M, N, K, win):
+    rng = np.random.default_rng(M + N + K)
+    qx = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    m0, mt, n0, nt = win
+    p = w8a8.debug_kblock_partials(_dev(qx), _dev(qw), m0, mt, n0, nt)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), oracle.kblock_partials(qx, qw, m0, mt, n0, nt))
+
+
+def test_partials_extremes():
+    qx = np.full((128, 256), 127, np.int8)
+    qw = np.full((128, 256), -127, np.int8)
+    qw[:, 128:] = 127
+    p = w8a8.debug_kblock_partials(_dev(qx), _dev(qw), 0, 128, 0, 128).cpu().numpy()
+    assert np.all(p[:, :, 0] == -2064512) and np.all(p[:, :, 1] == 2064512)
+
+
+def _gemm_case(M, N, K, seed, bias=False):
+    x = random_bf16(seed, (M, K))
+    w = random_bf16(seed + 1, (N, K), 0.02)
+    b = random_bf16(seed + 2, (N,), 0.5) if bias else None
+    qx, sx = oracle.quantize_block(x)
+    qw, sw = oracle.quantize_block(w)
+    y = w8a8.gemm_blockscale(_dev(qx), _dev(sx), _dev(qw), _dev(sw),
+                             bias=None if b is None else to_dev_bf16(b))
+    torch.cuda.synchronize()
+    yo = oracle.linear_int8(qx, sx, qw, sw, bias=b)
+    return assert_bf16_close(bf16_bits(y), yo, f"gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,bias", [(256, 256, 256, False), (384, 640, 512, True),
+                                        (1024, 256, 1024, False), (128, 1152, 384, True)])
+def test_gemm_vs_oracle(M, N, K, bias):
+    _gemm_case(M, N, K, M * 7 + N, bias)
+
+
+def test_gemm_zero_rows():
+    # an all-zero activation block row gives exactly-zero output rows
+    x = random_bf16(9, (256, 256))
+    x[128:] = 0
+    w = random_bf16(10, (256, 256), 0.02)
+    qx, sx = oracle.quantize_block(x)
+    qw, sw = oracle.quantize_block(w)
+    y = bf16_bits(w8a8.gemm_blockscale(_dev(qx), _dev(sx), _dev(qw), _dev(sw)))
+    assert not y[128:].any()
+    assert_bf16_close(y, oracle.linear_int8(qx, sx, qw, sw), "zero rows")

@@ -1,0 +1,97 @@
+"""Host-side checks of libw8a8.so that need no GPU.
+
+The library loads, exports every entry point include/w8a8.h declares, its
+guard matches the pages' rule on the golden table, and argument errors that
+are decided before any device access come back as status codes.  No call
+here reaches a kernel or a device query.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, load_golden
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_quantized_int8_amd import _lib
+    from block_quantized_int8_amd import build as b
+    if not os.path.exists(b.OUT):
+        b.build()
+    return _lib.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "w8a8.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    from block_quantized_int8_amd import _lib
+    declared = _declared()
+    assert len(declared) >= 9
+    assert sorted(_lib.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_route_golden(L):
+    g = load_golden("route_cases.json")
+    for dt, M, K, N, hq, want, note in g["cases"]:
+        assert L.w8a8_route(dt, M, K, N, hq) == want, note
+
+
+def test_route_matches_oracle_exhaustive_small(L):
+    import oracle
+    for dt in (0, 1, 2, 5):
+        for M in (1, 127, 128, 256, 4000):
+            for K in (128, 130, 4096):
+                for N in (64, 128, 2048):
+                    for hq in (0, 1):
+                        assert L.w8a8_route(dt, M, K, N, hq) == oracle.route(dt, M, K, N, hq)
+
+
+def test_status_strings(L):
+    assert L.w8a8_status_string(0) == b"W8A8_OK"
+    assert L.w8a8_status_string(1) == b"W8A8_ERR_INVALID_ARG"
+    assert L.w8a8_status_string(2) == b"W8A8_ERR_UNSUPPORTED"
+    assert L.w8a8_status_string(3) == b"W8A8_ERR_HIP"
+    assert L.w8a8_status_string(42) == b"W8A8_UNKNOWN_STATUS"
+    assert L.w8a8_last_hip_error() == 0
+
+
+def test_workspace_bytes(L):
+    assert L.w8a8_linear_workspace_bytes(256, 256) == 65536 + 256
+    assert L.w8a8_linear_workspace_bytes(32768, 4096) == 32768 * 4096 + 32768 // 128 * 32 * 4
+    assert L.w8a8_linear_workspace_bytes(4000, 4096) == 0
+    assert L.w8a8_linear_workspace_bytes(128, 0) == 0
+
+
+def test_host_decided_errors(L):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+    null = None
+    # null or non-positive arguments
+    assert L.w8a8_quantize_weight(null, 128, 128, fake, fake, null) == 1
+    assert L.w8a8_quantize_act(fake, 0, 128, fake, fake, null) == 1
+    # strict quantizers: shapes that are not multiples of 128
+    assert L.w8a8_quantize_act(fake, 130, 128, fake, fake, null) == 2
+    assert L.w8a8_quantize_weight(fake, 128, 4000, fake, fake, null) == 2
+    # misaligned pointer on a strict entry point
+    assert L.w8a8_quantize_act(ctypes.c_void_p(0x1002), 128, 128, fake, fake, null) == 2
+    assert L.w8a8_gemm_blockscale(fake, fake, fake, fake, null, 4000, 128, 128, fake, null) == 2
+    assert L.w8a8_gemm_blockscale(null, fake, fake, fake, null, 128, 128, 128, fake, null) == 1
+    # linear: missing weight copy, unknown dtype, half a quantized weight
+    path = ctypes.c_int(-7)
+    assert L.w8a8_linear(fake, 0, 128, 128, 128, null, null, null, null, fake, null, 0, null,
+                         ctypes.byref(path)) == 1
+    assert L.w8a8_linear(fake, 9, 128, 128, 128, fake, null, null, null, fake, null, 0, null,
+                         ctypes.byref(path)) == 1
+    assert L.w8a8_linear(fake, 0, 128, 128, 128, fake, fake, null, null, fake, null, 0, null,
+                         ctypes.byref(path)) == 1
+    assert path.value == -7  # untouched on early errors
+    # partials window checks
+    assert L.w8a8_debug_kblock_partials(fake, fake, 256, 256, 256, 128, 256, 0, 128, fake, null) == 1
+    assert L.w8a8_debug_kblock_partials(fake, fake, 256, 256, 256, 64, 128, 0, 128, fake, null) == 2
