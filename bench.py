@@ -1,0 +1,269 @@
+"""Benchmark of the guarded W8A8 block-quantized linear on one MI355X.
+
+A step is one call of the guarded linear (w8a8_linear) on the
+attention-projection workload: X[32768, 4096] bf16 with heavy-tailed
+activations (1% of channels x20), W[4096, 4096] bf16 ~ N(0, 0.02^2), seed 2.
+On this shape the guard takes the INT8 path, so a step is the dynamic
+128x128 activation quantization followed by the INT8 GEMM with per-K-block
+dequantization and bf16 output.  The weight is quantized once, before
+timing (static weights).  Inputs are resident in HBM when timing starts.
+
+Printed: one JSON line with the whole-step throughput (value, in TOPS of
+2*M*N*K per step), the per-kernel figures measured with HIP events on the
+stream the kernels run on, the roofline of the dominant kernel (the GEMM,
+bound by the INT8 MFMA peak) and the CPU oracle timed on a bounded sample of
+the same workload on this host.
+
+Modes for profiling runs: --only gemm|quantize|linear launches just that
+work for --steps iterations (no oracle); --copy-calibration runs a plain
+1 GiB device copy used to scale the HBM byte counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+M, N, K = 32768, 4096, 4096
+PEAK_INT8_TOPS = 256 * 8192 * 2.4e9 / 1e12   # 5033.2: 256 CUs x 8192 int8 ops/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "INT8 GEMM TOPS + % of INT8 MFMA peak; quantize GB/s (M=32768,K=N=4096)"
+# algorithmic bytes of the activation quantization: read bf16 X, write int8
+# qX and one fp32 scale per 128x128 block
+QUANT_BYTES = M * K * 2 + M * K * 1 + (M // 128) * (K // 128) * 4
+# algorithmic bytes of the GEMM: read qX, qW and both scale grids, write bf16 Y
+GEMM_BYTES = M * K + N * K + (M // 128 + N // 128) * (K // 128) * 4 + M * N * 2
+GEMM_OPS = 2 * M * N * K
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_i8_attnproj.json")
+GEMM_SOURCE = os.path.join(ROOT, "block_quantized_int8_amd", "csrc", "gemm_i8_blockscale.hip")
+CPU_SAMPLE_BLOCKS = 64      # 128-row blocks of X the oracle processes (8192 of 32768 rows)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or
+    None when absent or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(GEMM_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def ensure_built():
+    from block_quantized_int8_amd import build as b
+    if not os.path.exists(b.OUT):
+        b.build()
+
+
+def make_inputs(dev):
+    import numpy as np
+    import torch
+    from block_quantized_int8_amd.workloads import c3
+    d = c3(M)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(d["w"].view(np.int16)).to(dev).view(torch.bfloat16)
+    return d, x, w
+
+
+def cpu_baseline(d):
+    """The oracle (untuned) on the first CPU_SAMPLE_BLOCKS row-blocks of X:
+    quantize those rows and compute their full output rows."""
+    import numpy as np
+    import oracle
+    from oracle import build as ob
+    if not os.path.exists(ob.OUT):
+        ob.build()
+    rows = CPU_SAMPLE_BLOCKS * 128
+    xs = np.ascontiguousarray(d["x"][:rows])
+    t0 = time.perf_counter()
+    qw, sw = oracle.quantize_block(d["w"])            # static: excluded below
+    t1 = time.perf_counter()
+    qx, sx = oracle.quantize_block(xs)
+    oracle.linear_int8(qx, sx, qw, sw)
+    t2 = time.perf_counter()
+    secs = t2 - t1
+    ops = 2 * rows * N * K
+    return {"value": ops / secs / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(secs, 3),
+            "sample": f"first {rows} of {M} rows of X (quantize + full output rows), "
+                      f"N=K={K}; weight quantization ({t1 - t0:.2f} s) excluded as static"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["gemm", "quantize", "linear"], default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the layer shards by rows with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    ensure_built()
+    import block_quantized_int8_amd as w8a8
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.steps} copies of {n} bytes")
+        return
+
+    t_gen = time.perf_counter()
+    d, x, w = make_inputs(dev)
+    log(f"inputs ready ({time.perf_counter() - t_gen:.1f} s): X {tuple(x.shape)}, W {tuple(w.shape)}")
+    layer = w8a8.W8A8Linear(w)                       # static weight quantization
+    qw, sw = layer.qweight, layer.wscale
+    ws = torch.empty(w8a8.workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qx = ws[:M * K].view(torch.int8).view(M, K)
+    sx_off = (M * K + 255) // 256 * 256
+    sx = ws[sx_off:sx_off + (M // 128) * (K // 128) * 4].view(torch.float32).view(M // 128, K // 128)
+
+    def step():
+        _, path = w8a8.linear(x, w, qw, sw, out=y, workspace=ws)
+        return path
+
+    if args.only:
+        fn = {"linear": step,
+              "quantize": lambda: w8a8.quantize_act(x, qx, sx),
+              "gemm": lambda: w8a8.gemm_blockscale(qx, sx, qw, sw, out=y)}[args.only]
+        step()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"--only {args.only}: {args.steps} launches done")
+        return
+
+    assert step() == w8a8.PATH_INT8
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"step: {ms_step * 1e3:.1f} us (events), wall {wall / args.steps * 1e6:.1f} us")
+
+    # ---- per-kernel durations: events between the two launches of each
+    # step, on the stream the kernels run on (torch's current stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        w8a8.quantize_act(x, qx, sx)
+        ev[i][1].record()
+        w8a8.gemm_blockscale(qx, sx, qw, sw, out=y)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+
+    # quantize with the 256 MiB last-level cache flushed before each launch
+    # by READING 1 GiB (a write-based flush would leave dirty lines whose
+    # write-back competes with the timed kernel)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    qt = []
+    for i in range(args.steps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        w8a8.quantize_act(x, qx, sx)
+        b.record()
+        qt.append((a, b))
+    torch.cuda.synchronize()
+    quant_ms = sum(a.elapsed_time(b) for a, b in qt) / args.steps
+    del flush
+
+    gemm_tops = GEMM_OPS / (gemm_ms * 1e-3) / 1e12
+    quant_gbs = QUANT_BYTES / (quant_ms * 1e-3) / 1e9
+    value = GEMM_OPS / (ms_step * 1e-3) / 1e12
+    log(f"gemm {gemm_ms * 1e3:.1f} us = {gemm_tops:.0f} TOPS ({gemm_tops / PEAK_INT8_TOPS:.1%}); "
+        f"quantize {quant_ms * 1e3:.1f} us = {quant_gbs:.0f} GB/s ({quant_gbs / PEAK_HBM_GBS:.1%})")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on its sample ...")
+        cpu = cpu_baseline(d)
+        log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GOPS on {cpu['cores']} threads, {cpu['seconds']} s")
+
+    traffic = load_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "attention-projection W8A8 linear, heavy-tailed activations "
+                               "(1% of K channels x20), seed 2",
+                   "M": M, "N": N, "K": K, "block": 128, "path": "int8",
+                   "step": "w8a8_linear = activation quantize + INT8 block-scale GEMM"},
+        "gemm_tops": round(gemm_tops, 1),
+        "gemm_frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4),
+        "gemm_us": round(gemm_ms * 1e3, 2),
+        "quantize_gbs": round(quant_gbs, 1),
+        "quantize_frac_of_hbm": round(quant_gbs / PEAK_HBM_GBS, 4),
+        "quantize_us": round(quant_ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_i8_blockscale",
+                     "achieved": round(gemm_tops, 1), "peak": round(PEAK_INT8_TOPS, 1),
+                     "unit": "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": GEMM_BYTES, "ops_per_launch": GEMM_OPS},
+        "roofline_quantize": {"bound": "hbm", "kernel": "quantize_block",
+                              "achieved": round(quant_gbs, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes": QUANT_BYTES},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -59,25 +59,33 @@ def workspace_bytes(M: int, K: int) -> int:
     return int(lib().w8a8_linear_workspace_bytes(int(M), int(K)))
 
 
-def _quantize(fn, name, x):
+def _quantize(fn, name, x, q, s):
     _need_cuda(name, x, torch.bfloat16)
     if x.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
     R, C = x.shape
-    q = torch.empty((R, C), dtype=torch.int8, device=x.device)
-    s = torch.empty((max(R // BLOCK, 1), max(C // BLOCK, 1)), dtype=torch.float32, device=x.device)
+    sshape = (max(R // BLOCK, 1), max(C // BLOCK, 1))
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    _need_cuda("q", q, torch.int8)
+    _need_cuda("s", s, torch.float32)
+    if q.numel() != R * C or s.numel() != sshape[0] * sshape[1]:
+        raise ValueError("output buffers have the wrong size")
     check(fn.__name__, fn(_ptr(x), R, C, _ptr(q), _ptr(s), _stream(x.device)))
     return q, s
 
 
-def quantize_weight(w: torch.Tensor):
+def quantize_weight(w: torch.Tensor, q=None, s=None):
     """Static 128x128 block INT8 quantization of a bf16 weight [N, K]."""
-    return _quantize(lib().w8a8_quantize_weight, "w", w)
+    return _quantize(lib().w8a8_quantize_weight, "w", w, q, s)
 
 
-def quantize_act(x: torch.Tensor):
-    """Dynamic 128x128 block INT8 quantization of bf16 activations [M, K]."""
-    return _quantize(lib().w8a8_quantize_act, "x", x)
+def quantize_act(x: torch.Tensor, q=None, s=None):
+    """Dynamic 128x128 block INT8 quantization of bf16 activations [M, K]
+    (into ``q``/``s`` when given)."""
+    return _quantize(lib().w8a8_quantize_act, "x", x, q, s)
 
 
 def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):

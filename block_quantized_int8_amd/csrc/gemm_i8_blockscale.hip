@@ -10,23 +10,41 @@
 // inference stack, W8A8 paragraph, which names this repeated scaling along
 // the reduction as the block form's cost and applies bias in the epilogue).
 //
-// Structure: one workgroup (4 wavefronts) per 128x128 output tile; one
-// K-block (128 deep) per main-loop iteration.  Both operands are K-contiguous
-// ("NT"), so every MFMA operand fragment is one 16-byte LDS read.  Tiles of
-// qx and qw (16 KiB each) are double-buffered in LDS; the next K-block's
-// global loads are issued before the current one's MFMAs.  LDS rows are 128
-// bytes with the 16-byte chunk index XOR-swizzled by (row & 7), so the 8
-// lanes that read one chunk column of 8 consecutive rows hit distinct banks.
+// Work decomposition
+//   * one workgroup (8 wavefronts, 2 per SIMD) per 256x256 output tile; one
+//     128-deep K-block per main-loop iteration;
+//   * each wavefront owns a 128 (n) x 64 (m) sub-tile = 4 x 2 MFMA tiles of
+//     32x32, which lies inside a single 128x128 scale block of Y, so the
+//     combined scale sx*sw is one scalar per wavefront and K-block;
+//   * v_mfma_i32_32x32x32_i8 gives the exact int32 sum of a 32-deep slice;
+//     four of them (the first with a zero C operand) give P for one K-block,
+//     which is converted to fp32 and fused into the fp32 accumulator with one
+//     FMA by that scale.  The fp32 accumulators (128 per lane) must stay in
+//     VGPRs because this per-K-block dequantization runs on the VALU; that is
+//     what caps the wavefront tile at 128x64.
 //
-// v_mfma_i32_32x32x32_i8 produces the exact int32 sum of one 32-deep slice;
-// four of them (accumulating in int32, the first with a zero C operand) give
-// P for one K-block.  P is converted to fp32 and fused into the fp32
-// accumulator with one FMA by the combined block scale (a scalar per
-// (m-block, n-block, K-block), identical across the tile).
+// Data movement
+//   * both operands are K-contiguous (Y = X W^T, "NT"): every MFMA operand
+//     fragment is one 16-byte LDS read (lane l: row l%32, k-half l/32);
+//   * operand tiles go from global memory straight into LDS with
+//     global_load_lds_dwordx4 (no VGPR staging), double-buffered: 2 stages x
+//     (256 + 256) rows x 128 bytes = 128 KiB.  The next K-block's loads are
+//     in flight while the current one is multiplied;
+//   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
+//     (row & 7); the direct loads write 1 KiB lane-linearly, so each lane
+//     fetches the global chunk that belongs at its LDS slot;
+//   * workgroups are dispatched round-robin over the 8 XCDs; the tile index
+//     is remapped so each XCD works on a contiguous range of tiles, ordered
+//     in groups of 8 m-tiles sweeping n, so tiles resident on one XCD share
+//     operand panels in its L2.
+//
+// Edges: M, N, K are multiples of 128 but not necessarily of 256; rows past
+// the end of a partial tile are clamped to the last valid row for loading,
+// and wavefronts whose sub-tile lies outside the output skip their work.
 //
 // The weight fragment is the MFMA "A" operand and the activation fragment
-// the "B" operand, so each lane ends up holding 4 consecutive output columns
-// n of one row m per register group: the epilogue writes 8-byte bf16 quads.
+// the "B" operand, so each lane holds 4 consecutive output columns n of one
+// row m per register group and the epilogue writes 8-byte bf16 quads.
 //
 // kPartials = true is the test epilogue: the same main loop stores P itself.
 #include "w8a8_internal.h"
@@ -34,170 +52,197 @@
 namespace w8a8 {
 namespace {
 
-constexpr int kTile = 128;   // output tile edge (M and N)
-constexpr int kThreads = 256;
-constexpr int kLdsTile = kTile * kBlock;  // bytes per operand tile per stage
+constexpr int kTileM = 256, kTileN = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kWaveM = 64, kWaveN = 128;
+constexpr int kStage = (kTileM + kTileN) * kBlock;  // bytes per pipeline stage
+constexpr int kGroupM = 8;
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) void *global_ptr_t;
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kBlock + ((chunk ^ (row & 7)) << 4);
-}
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBlock + ((chunk ^ (row & 7)) << 4); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+struct Problem {
+    const int8_t *qx;
+    const float *sx;
+    const int8_t *qw;
+    const float *sw;
+    const uint16_t *bias;
+    uint16_t *y;
+    int32_t *partials;
+    int64_t N, K;
+    int64_t m_begin, m_end, n_begin, n_end;  // output window (multiples of 128)
+    int tiles_m, tiles_n;
+};
 
 template <bool kPartials>
-__global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
-    const int8_t *__restrict__ qx, const float *__restrict__ sx, const int8_t *__restrict__ qw,
-    const float *__restrict__ sw, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
-    int64_t N, int64_t K, int tiles_m, int tiles_n, int mb0, int nb0, int32_t *__restrict__ partials,
-    int64_t part_nt) {
-    __shared__ __attribute__((aligned(16))) int8_t lds[2][2][kLdsTile];
+__global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(const Problem p) {
+    __shared__ __attribute__((aligned(1024))) int8_t lds[2 * kStage];
 
-    // Tile order: groups of 8 m-tiles sweep all n-tiles, m fastest inside a
-    // group, so concurrently resident workgroups share operand panels.
-    const int t = blockIdx.x;
-    constexpr int kGroup = 8;
-    const int group_size = kGroup * tiles_n;
+    // ---- tile index: XCD-contiguous ranges, then grouped m-fastest order
+    const int nwg = (int)gridDim.x;
+    int t = (int)blockIdx.x;
+    if ((nwg & 7) == 0) t = (t & 7) * (nwg >> 3) + (t >> 3);
+    const int group_size = kGroupM * p.tiles_n;
     const int g = t / group_size;
-    const int first_m = g * kGroup;
-    const int gm = min(tiles_m - first_m, kGroup);
+    const int first_m = g * kGroupM;
+    const int gm = min(p.tiles_m - first_m, kGroupM);
     const int in_group = t - g * group_size;
-    const int mb = mb0 + first_m + in_group % gm;
-    const int nb = nb0 + in_group / gm;
+    const int64_t m_org = p.m_begin + (int64_t)(first_m + in_group % gm) * kTileM;
+    const int64_t n_org = p.n_begin + (int64_t)(in_group / gm) * kTileN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;  // wave's 64x64 quadrant (m, n)
-    const int64_t KB = K / kBlock;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int64_t K = p.K;
+    const int KB = (int)(K / kBlock);
 
-    // global -> LDS copy assignment: 1024 16-byte chunks per operand tile
-    const int8_t *gx = qx + (int64_t)mb * kTile * K;
-    const int8_t *gw = qw + (int64_t)nb * kTile * K;
-    int64_t g_off[4];
-    int l_off[4];
+    // ---- direct global->LDS loads: wave w fills rows [32w, 32w+32) of both
+    // operand tiles, 8 rows (1 KiB) per instruction
+    const int lrow0 = wave * 32 + (lane >> 3);
+    int64_t xoff[4], woff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int c = tid + i * kThreads;
-        const int row = c >> 3, ch = c & 7;
-        g_off[i] = (int64_t)row * K + ch * 16;
-        l_off[i] = swz(row, ch);
+        const int r = lrow0 + i * 8;
+        const int chunk = (lane & 7) ^ (r & 7);
+        const int64_t xr = min(m_org + r, p.m_end - 1);
+        const int64_t wr = min(n_org + r, p.n_end - 1);
+        xoff[i] = xr * K + chunk * 16;
+        woff[i] = wr * K + chunk * 16;
     }
-
-    i32x4 rx[4], rw[4];
-    auto load_tiles = [&](int64_t kb) {
+    auto issue_loads = [&](int stage, int kb) {
+        int8_t *xs = lds + stage * kStage + wave * 32 * kBlock;
+        int8_t *ws = xs + kTileM * kBlock;
+        const int64_t ko = (int64_t)kb * kBlock;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            rx[i] = *reinterpret_cast<const i32x4 *>(gx + g_off[i] + kb * kBlock);
-            rw[i] = *reinterpret_cast<const i32x4 *>(gw + g_off[i] + kb * kBlock);
-        }
-    };
-    auto store_tiles = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<i32x4 *>(&lds[buf][0][l_off[i]]) = rx[i];
-            *reinterpret_cast<i32x4 *>(&lds[buf][1][l_off[i]]) = rw[i];
+            __builtin_amdgcn_global_load_lds((global_ptr_t)(p.qx + xoff[i] + ko),
+                                             (lds_ptr_t)(xs + i * 8 * kBlock), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((global_ptr_t)(p.qw + woff[i] + ko),
+                                             (lds_ptr_t)(ws + i * 8 * kBlock), 16, 0, 0);
         }
     };
 
-    f32x16 acc[2][2];
+    const bool active = (m_org + wm * kWaveM < p.m_end) && (n_org + wn * kWaveN < p.n_end);
+    const int64_t mblk = (m_org + wm * kWaveM) / kBlock;
+    const int64_t nblk = (n_org + wn * kWaveN) / kBlock;
+    const float *sxr = kPartials ? nullptr : p.sx + mblk * KB;
+    const float *swr = kPartials ? nullptr : p.sw + nblk * KB;
+
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const float *sxr = kPartials ? nullptr : sx + (int64_t)mb * KB;
-    const float *swr = kPartials ? nullptr : sw + (int64_t)nb * KB;
-
-    load_tiles(0);
-    store_tiles(0);
+    issue_loads(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    const int frag_row = lane & 31, frag_half = lane >> 5;
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const int buf = (int)(kb & 1);
-        if (kb + 1 < KB) load_tiles(kb + 1);
+    const int frow = lane & 31, fhalf = lane >> 5;
+    for (int kb = 0; kb < KB; ++kb) {
+        const int stage = kb & 1;
+        if (kb + 1 < KB) issue_loads(stage ^ 1, kb + 1);
 
-        i32x4 fx[2][4], fw[2][4];
+        if (active) {
+            const int8_t *xs = lds + stage * kStage;
+            const int8_t *ws = xs + kTileM * kBlock;
+            i32x4 fx[2][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int row = wm * 64 + j * 32 + frag_row;
-                fx[j][kk] = *reinterpret_cast<const i32x4 *>(&lds[buf][0][swz(row, kk * 2 + frag_half)]);
-            }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int row = wn * 64 + i * 32 + frag_row;
-                fw[i][kk] = *reinterpret_cast<const i32x4 *>(&lds[buf][1][swz(row, kk * 2 + frag_half)]);
-            }
-
-        float scale = 0.0f;
-        if constexpr (!kPartials) scale = sxr[kb] * swr[kb];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                i32x16 p = {0};
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    p = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i][kk], fx[j][kk], p, 0, 0, 0);
-                if constexpr (kPartials) {
-                    const int64_t m = (int64_t)(mb - mb0) * kTile + wm * 64 + j * 32 + frag_row;
+                    fx[j][kk] = *reinterpret_cast<const i32x4 *>(
+                        xs + swz(wm * kWaveM + j * 32 + frow, kk * 2 + fhalf));
+            float scale = 0.0f;
+            if constexpr (!kPartials) scale = sxr[kb] * swr[kb];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int64_t n = (int64_t)(nb - nb0) * kTile + wn * 64 + i * 32 +
-                                          (r >> 2) * 8 + frag_half * 4 + (r & 3);
-                        partials[(m * part_nt + n) * KB + kb] = p[r];
+            for (int i = 0; i < 4; ++i) {
+                i32x4 fw[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    fw[kk] = *reinterpret_cast<const i32x4 *>(
+                        ws + swz(wn * kWaveN + i * 32 + frow, kk * 2 + fhalf));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    i32x16 pk = {0};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        pk = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk], fx[j][kk], pk, 0, 0, 0);
+                    if constexpr (kPartials) {
+                        const int64_t m = m_org - p.m_begin + wm * kWaveM + j * 32 + frow;
+                        const int64_t nt = p.n_end - p.n_begin;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int64_t n = n_org - p.n_begin + wn * kWaveN + i * 32 + (r >> 2) * 8 +
+                                              fhalf * 4 + (r & 3);
+                            p.partials[(m * nt + n) * KB + kb] = pk[r];
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[i][j][r] = __builtin_fmaf((float)pk[r], scale, acc[i][j][r]);
                     }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[i][j][r] = __builtin_fmaf((float)p[r], scale, acc[i][j][r]);
                 }
             }
-
-        if (kb + 1 < KB) store_tiles(buf ^ 1);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
     if constexpr (!kPartials) {
+        if (!active) return;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int64_t m = (int64_t)mb * kTile + wm * 64 + j * 32 + frag_row;
+                const int64_t m = m_org + wm * kWaveM + j * 32 + frow;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t n = (int64_t)nb * kTile + wn * 64 + i * 32 + q * 8 + frag_half * 4;
+                    const int64_t n = n_org + wn * kWaveN + i * 32 + q * 8 + fhalf * 4;
                     float v0 = acc[i][j][q * 4 + 0], v1 = acc[i][j][q * 4 + 1];
                     float v2 = acc[i][j][q * 4 + 2], v3 = acc[i][j][q * 4 + 3];
-                    if (bias) {
-                        const u32x2 b = *reinterpret_cast<const u32x2 *>(bias + n);
-                        v0 += bf16_to_f32((uint16_t)(b.x & 0xFFFF));
-                        v1 += bf16_to_f32((uint16_t)(b.x >> 16));
-                        v2 += bf16_to_f32((uint16_t)(b.y & 0xFFFF));
-                        v3 += bf16_to_f32((uint16_t)(b.y >> 16));
+                    if (p.bias) {
+                        const u32x2 b = *reinterpret_cast<const u32x2 *>(p.bias + n);
+                        v0 += bf16_to_f32(b.x & 0xFFFFu);
+                        v1 += bf16_to_f32(b.x >> 16);
+                        v2 += bf16_to_f32(b.y & 0xFFFFu);
+                        v3 += bf16_to_f32(b.y >> 16);
                     }
                     u32x2 out;
                     out.x = pack_bf16x2(v0, v1);
                     out.y = pack_bf16x2(v2, v3);
-                    *reinterpret_cast<u32x2 *>(y + m * N + n) = out;
+                    *reinterpret_cast<u32x2 *>(p.y + m * p.N + n) = out;
                 }
             }
     }
+}
+
+template <bool kPartials>
+hipError_t launch(Problem p, hipStream_t stream) {
+    const int64_t tm = (p.m_end - p.m_begin + kTileM - 1) / kTileM;
+    const int64_t tn = (p.n_end - p.n_begin + kTileN - 1) / kTileN;
+    if (tm <= 0 || tn <= 0 || p.K < kBlock) return hipSuccess;
+    if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    gemm_i8_bs_kernel<kPartials><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -205,26 +250,17 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
 hipError_t launch_gemm_i8_blockscale(const int8_t *qx, const float *sx, const int8_t *qw,
                                      const float *sw, const uint16_t *bias, int64_t M, int64_t N,
                                      int64_t K, uint16_t *y, hipStream_t stream) {
-    const int64_t tm = M / kTile, tn = N / kTile;
-    if (tm <= 0 || tn <= 0 || K < kBlock) return hipSuccess;
-    if (tm * tn > 0x7FFFFFFF || tm > 0x7FFFFFFF || tn > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemm_i8_bs_kernel<false><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
-        qx, sx, qw, sw, bias, y, N, K, (int)tm, (int)tn, 0, 0, nullptr, 0);
-    return hipGetLastError();
+    Problem p{qx, sx, qw, sw, bias, y, nullptr, N, K, 0, M, 0, N, 0, 0};
+    return launch<false>(p, stream);
 }
 
 hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N,
                                   int64_t K, int64_t m0, int64_t mt, int64_t n0, int64_t nt,
                                   int32_t *partials, hipStream_t stream) {
     (void)M;
-    const int64_t tm = mt / kTile, tn = nt / kTile;
-    if (tm <= 0 || tn <= 0) return hipSuccess;
-    if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
     // the partials epilogue reads no scale, bias or output
-    gemm_i8_bs_kernel<true><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
-        qx, nullptr, qw, nullptr, nullptr, nullptr, N, K, (int)tm, (int)tn, (int)(m0 / kTile),
-        (int)(n0 / kTile), partials, nt);
-    return hipGetLastError();
+    Problem p{qx, nullptr, qw, nullptr, nullptr, nullptr, partials, N, K, m0, m0 + mt, n0, n0 + nt, 0, 0};
+    return launch<true>(p, stream);
 }
 
 }  // namespace w8a8
