@@ -27,11 +27,11 @@
 //   * both operands are K-contiguous (Y = X W^T, "NT"): every MFMA operand
 //     fragment is one 16-byte LDS read (lane l: row l%32, k-half l/32);
 //   * operand tiles go from global memory straight into LDS with
-//     global_load_lds_dwordx4 (no VGPR staging), double-buffered: 2 stages x
+//     buffer_load_dwordx4 ... lds (no VGPR staging), double-buffered: 2 stages x
 //     (256 + 256) rows x 128 bytes = 128 KiB.  The next K-block's loads are
 //     in flight while the current one is multiplied;
-//   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
-//     (row & 7); the direct loads write 1 KiB lane-linearly, so each lane
+//   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled (see
+//     swz_slot); the direct loads write 1 KiB lane-linearly, so each lane
 //     fetches the global chunk that belongs at its LDS slot;
 //   * workgroups are dispatched round-robin over the 8 XCDs; the tile index
 //     is remapped so each XCD works on a contiguous range of tiles, ordered
@@ -39,12 +39,18 @@
 //     operand panels in its L2.
 //
 // Edges: M, N, K are multiples of 128 but not necessarily of 256; rows past
-// the end of a partial tile are clamped to the last valid row for loading,
-// and wavefronts whose sub-tile lies outside the output skip their work.
+// the end of a partial tile read as zeros (buffer range check), and
+// wavefronts whose sub-tile lies outside the output skip their work.
+//
+// Within a wavefront the K-block loop is software-pipelined: the four MFMAs
+// of sub-tile s are interleaved with the 32 VALU ops that dequantize the
+// finished partial of sub-tile s-1, so the matrix core and the VALU work at
+// the same time.
 //
 // The weight fragment is the MFMA "A" operand and the activation fragment
 // the "B" operand, so each lane holds 4 consecutive output columns n of one
-// row m per register group and the epilogue writes 8-byte bf16 quads.
+// row m per register group.  The output goes through LDS (free after the
+// main loop) so that Y is written in whole 256-byte row segments.
 //
 // kPartials = true is the test epilogue: the same main loop stores P itself.
 #include "w8a8_internal.h"
@@ -64,9 +70,15 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
-typedef __attribute__((address_space(1))) void *global_ptr_t;
+// buffer descriptor word 3 for raw (untyped) dword buffer access on gfx9 parts
+constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBlock + ((chunk ^ (row & 7)) << 4); }
+// LDS slot of 16-byte chunk `chunk` in operand row `row`: XOR with (row & 7)
+// and bit 3 of the row, so both 8 consecutive rows (32 banks x 4 bytes) and
+// 16 consecutive rows (64 banks, even/odd rows in opposite 128-byte halves)
+// read one chunk column without bank conflicts.  Self-inverse in `chunk`.
+__device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBlock + (swz_slot(row, chunk) << 4); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
@@ -75,21 +87,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Sizes of one launch.  The tensors are separate __restrict__ kernel
+// arguments so the compiler can prove the scale grids read-only and fetch
+// them with scalar loads (a vector load would be ordered behind the
+// in-flight operand prefetch in the same vmcnt queue).
 struct Problem {
-    const int8_t *qx;
-    const float *sx;
-    const int8_t *qw;
-    const float *sw;
-    const uint16_t *bias;
-    uint16_t *y;
-    int32_t *partials;
     int64_t N, K;
     int64_t m_begin, m_end, n_begin, n_end;  // output window (multiples of 128)
     int tiles_m, tiles_n;
 };
 
+// Dequantize one quarter (elements 4*part .. 4*part+3) of a finished K-block
+// partial into the accumulator: 8 VALU ops, issued between two MFMAs.
+__device__ __forceinline__ void dequant_quarter(f32x16 &acc, const i32x16 &pk, float scale, int part) {
+#pragma unroll
+    for (int r = part * 4; r < part * 4 + 4; ++r) acc[r] = __builtin_fmaf((float)pk[r], scale, acc[r]);
+}
+
+// Buffer resource for `rows` rows of K bytes starting at `base`: loads past
+// the last row return zeros (raw buffer range check), which is how partial
+// edge tiles are handled without clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const int8_t *base, int64_t rows, int64_t K) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(base), (short)0, (int)(rows * K),
+                                             kRsrcWord3);
+}
+
 template <bool kPartials>
-__global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(const Problem p) {
+__global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
+    const int8_t *__restrict__ qx, const float *__restrict__ sx, const int8_t *__restrict__ qw,
+    const float *__restrict__ sw, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
+    int32_t *__restrict__ partials, const Problem p) {
     __shared__ __attribute__((aligned(1024))) int8_t lds[2 * kStage];
 
     // ---- tile index: XCD-contiguous ranges, then grouped m-fastest order
@@ -104,102 +131,118 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(const Problem p) {
     const int64_t m_org = p.m_begin + (int64_t)(first_m + in_group % gm) * kTileM;
     const int64_t n_org = p.n_begin + (int64_t)(in_group / gm) * kTileN;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wn = wave & 1, wm = wave >> 1;
     const int64_t K = p.K;
     const int KB = (int)(K / kBlock);
 
-    // ---- direct global->LDS loads: wave w fills rows [32w, 32w+32) of both
-    // operand tiles, 8 rows (1 KiB) per instruction
-    const int lrow0 = wave * 32 + (lane >> 3);
-    int64_t xoff[4], woff[4];
+    // ---- operand loads, global -> LDS: wave w fills rows [32w, 32w+32) of
+    // both tiles, 8 rows (1 KiB, lane-linear in LDS) per instruction; row
+    // lrow + 8i for instruction i.  Lane l writes LDS slot l%8, which holds
+    // global chunk swz_slot(row, l%8).  That slot pattern depends on row bit
+    // 3, so even and odd instructions need different per-lane offsets; the
+    // rest (row block, K-block) is a scalar offset, the same for both operands.
+    const __amdgpu_buffer_rsrc_t xr = tile_rsrc(qx + m_org * K, min((int64_t)kTileM, p.m_end - m_org), K);
+    const __amdgpu_buffer_rsrc_t wr = tile_rsrc(qw + n_org * K, min((int64_t)kTileN, p.n_end - n_org), K);
+    const int lrow = wave * 32 + (lane >> 3);
+    uint32_t voff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = lrow0 + i * 8;
-        const int chunk = (lane & 7) ^ (r & 7);
-        const int64_t xr = min(m_org + r, p.m_end - 1);
-        const int64_t wr = min(n_org + r, p.n_end - 1);
-        xoff[i] = xr * K + chunk * 16;
-        woff[i] = wr * K + chunk * 16;
-    }
+    for (int b = 0; b < 2; ++b)
+        voff[b] = (uint32_t)(lrow * K) + (uint32_t)(swz_slot(lrow + 8 * b, lane & 7) * 16);
     auto issue_loads = [&](int stage, int kb) {
         int8_t *xs = lds + stage * kStage + wave * 32 * kBlock;
         int8_t *ws = xs + kTileM * kBlock;
-        const int64_t ko = (int64_t)kb * kBlock;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_global_load_lds((global_ptr_t)(p.qx + xoff[i] + ko),
-                                             (lds_ptr_t)(xs + i * 8 * kBlock), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((global_ptr_t)(p.qw + woff[i] + ko),
-                                             (lds_ptr_t)(ws + i * 8 * kBlock), 16, 0, 0);
+            const uint32_t so = (uint32_t)(kb * kBlock) + (uint32_t)(i * 8 * K);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xs + i * 8 * kBlock), 16, voff[i & 1], so,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(ws + i * 8 * kBlock), 16, voff[i & 1], so,
+                                                     0, 0);
         }
     };
 
     const bool active = (m_org + wm * kWaveM < p.m_end) && (n_org + wn * kWaveN < p.n_end);
     const int64_t mblk = (m_org + wm * kWaveM) / kBlock;
     const int64_t nblk = (n_org + wn * kWaveN) / kBlock;
-    const float *sxr = kPartials ? nullptr : p.sx + mblk * KB;
-    const float *swr = kPartials ? nullptr : p.sw + nblk * KB;
+    const float *sxr = kPartials ? nullptr : sx + mblk * KB;
+    const float *swr = kPartials ? nullptr : sw + nblk * KB;
 
-    f32x16 acc[4][2];
+    // sub-tile s = 2*i + j: weight rows 32i.., activation rows 32j.. of the wave tile
+    f32x16 acc[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+    i32x16 pk[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) pk[1][r] = 0;
+    float prev_scale = 0.0f;  // scale of the partial carried in pk[1]
+
+    // fragment read addresses: row (32-aligned base) + frow; the swizzle only
+    // depends on frow, so one per-lane byte offset per K-slice kk
+    const int frow = lane & 31, fhalf = lane >> 5;
+    int fofs[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) fofs[kk] = frow * kBlock + (swz_slot(frow, kk * 2 + fhalf) << 4);
 
     issue_loads(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    const int frow = lane & 31, fhalf = lane >> 5;
+    const i32x16 zero = {0};
     for (int kb = 0; kb < KB; ++kb) {
         const int stage = kb & 1;
         if (kb + 1 < KB) issue_loads(stage ^ 1, kb + 1);
 
         if (active) {
-            const int8_t *xs = lds + stage * kStage;
-            const int8_t *ws = xs + kTileM * kBlock;
-            i32x4 fx[2][4];
+            const int8_t *xs = lds + stage * kStage + wm * kWaveM * kBlock;
+            const int8_t *ws = lds + stage * kStage + kTileM * kBlock + wn * kWaveN * kBlock;
+            i32x4 fx[2][4], fw[2][4];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    fx[j][kk] = *reinterpret_cast<const i32x4 *>(
-                        xs + swz(wm * kWaveM + j * 32 + frow, kk * 2 + fhalf));
+                    fx[j][kk] = *reinterpret_cast<const i32x4 *>(xs + j * 32 * kBlock + fofs[kk]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) fw[0][kk] = *reinterpret_cast<const i32x4 *>(ws + fofs[kk]);
             float scale = 0.0f;
             if constexpr (!kPartials) scale = sxr[kb] * swr[kb];
+
+            // software pipeline: the MFMAs of sub-tile s run while the VALU
+            // dequantizes sub-tile s-1 (for s = 0: the last sub-tile of the
+            // previous K-block, carried across the barrier in pk[1])
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                i32x4 fw[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    fw[kk] = *reinterpret_cast<const i32x4 *>(
-                        ws + swz(wn * kWaveN + i * 32 + frow, kk * 2 + fhalf));
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    i32x16 pk = {0};
+            for (int s = 0; s < 8; ++s) {
+                const int i = s >> 1, j = s & 1;
+                if (j == 0 && i < 3) {
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        pk = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[kk], fx[j][kk], pk, 0, 0, 0);
-                    if constexpr (kPartials) {
-                        const int64_t m = m_org - p.m_begin + wm * kWaveM + j * 32 + frow;
-                        const int64_t nt = p.n_end - p.n_begin;
+                        fw[(i + 1) & 1][kk] =
+                            *reinterpret_cast<const i32x4 *>(ws + (i + 1) * 32 * kBlock + fofs[kk]);
+                }
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int64_t n = n_org - p.n_begin + wn * kWaveN + i * 32 + (r >> 2) * 8 +
-                                              fhalf * 4 + (r & 3);
-                            p.partials[(m * nt + n) * KB + kb] = pk[r];
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            acc[i][j][r] = __builtin_fmaf((float)pk[r], scale, acc[i][j][r]);
+                for (int kk = 0; kk < 4; ++kk) {
+                    pk[s & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i & 1][kk], fx[j][kk],
+                                                                      kk == 0 ? zero : pk[s & 1], 0, 0, 0);
+                    if constexpr (!kPartials) {
+                        if (s > 0)
+                            dequant_quarter(acc[s - 1], pk[(s - 1) & 1], scale, kk);
+                        else
+                            dequant_quarter(acc[7], pk[1], prev_scale, kk);
                     }
                 }
+                if constexpr (kPartials) {
+                    const int64_t m = m_org - p.m_begin + wm * kWaveM + j * 32 + frow;
+                    const int64_t nt = p.n_end - p.n_begin;
+                    int32_t *dst = partials + (m * nt + (n_org - p.n_begin) + wn * kWaveN + i * 32 +
+                                                 fhalf * 4) * KB + kb;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((r >> 2) * 8 + (r & 3)) * KB] = pk[s & 1][r];
+                }
             }
+            prev_scale = scale;
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -208,40 +251,63 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(const Problem p) {
     if constexpr (!kPartials) {
         if (!active) return;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int kk = 0; kk < 4; ++kk) dequant_quarter(acc[7], pk[1], prev_scale, kk);
+
+        // ---- epilogue through LDS (free after the last barrier): each wave
+        // writes its 64 (m) x 128 (n) bf16 tile as rows of 256 bytes with the
+        // 16-byte chunk index XOR-swizzled by (row & 15), then stores whole
+        // rows to Y with 16-byte, fully coalesced writes.
+        if (bias) {
+            const uint16_t *bp = bias + n_org + wn * kWaveN + fhalf * 4;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t m = m_org + wm * kWaveM + j * 32 + frow;
+            for (int s = 0; s < 8; ++s)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t n = n_org + wn * kWaveN + i * 32 + q * 8 + fhalf * 4;
-                    float v0 = acc[i][j][q * 4 + 0], v1 = acc[i][j][q * 4 + 1];
-                    float v2 = acc[i][j][q * 4 + 2], v3 = acc[i][j][q * 4 + 3];
-                    if (p.bias) {
-                        const u32x2 b = *reinterpret_cast<const u32x2 *>(p.bias + n);
-                        v0 += bf16_to_f32(b.x & 0xFFFFu);
-                        v1 += bf16_to_f32(b.x >> 16);
-                        v2 += bf16_to_f32(b.y & 0xFFFFu);
-                        v3 += bf16_to_f32(b.y >> 16);
-                    }
-                    u32x2 out;
-                    out.x = pack_bf16x2(v0, v1);
-                    out.y = pack_bf16x2(v2, v3);
-                    *reinterpret_cast<u32x2 *>(p.y + m * p.N + n) = out;
+                    const u32x2 b = *reinterpret_cast<const u32x2 *>(bp + (s >> 1) * 32 + q * 8);
+                    acc[s][q * 4 + 0] += bf16_to_f32(b.x & 0xFFFFu);
+                    acc[s][q * 4 + 1] += bf16_to_f32(b.x >> 16);
+                    acc[s][q * 4 + 2] += bf16_to_f32(b.y & 0xFFFFu);
+                    acc[s][q * 4 + 3] += bf16_to_f32(b.y >> 16);
                 }
+        }
+        int8_t *ot = lds + wave * (kWaveM * kWaveN * 2);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int i = s >> 1, j = s & 1;
+            const int row = j * 32 + frow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int chunk = i * 4 + q;  // 16-byte chunk (8 columns) inside the 128-column row
+                u32x2 out;
+                out.x = pack_bf16x2(acc[s][q * 4 + 0], acc[s][q * 4 + 1]);
+                out.y = pack_bf16x2(acc[s][q * 4 + 2], acc[s][q * 4 + 3]);
+                *reinterpret_cast<u32x2 *>(ot + row * 256 + ((chunk ^ (row & 15)) << 4) + fhalf * 8) = out;
             }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        const int c = lane & 15;
+        uint16_t *yrow = y + (m_org + wm * kWaveM) * p.N + n_org + wn * kWaveN + c * 8;
+#pragma unroll
+        for (int it = 0; it < kWaveM / 4; ++it) {
+            const int row = it * 4 + (lane >> 4);
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+            *reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N) = v;
+        }
     }
 }
 
 template <bool kPartials>
-hipError_t launch(Problem p, hipStream_t stream) {
+hipError_t launch(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                  const uint16_t *bias, uint16_t *y, int32_t *partials, Problem p, hipStream_t stream) {
     const int64_t tm = (p.m_end - p.m_begin + kTileM - 1) / kTileM;
     const int64_t tn = (p.n_end - p.n_begin + kTileN - 1) / kTileN;
     if (tm <= 0 || tn <= 0 || p.K < kBlock) return hipSuccess;
     if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
-    gemm_i8_bs_kernel<kPartials><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(p);
+    gemm_i8_bs_kernel<kPartials><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+        qx, sx, qw, sw, bias, y, partials, p);
     return hipGetLastError();
 }
 
@@ -250,8 +316,8 @@ hipError_t launch(Problem p, hipStream_t stream) {
 hipError_t launch_gemm_i8_blockscale(const int8_t *qx, const float *sx, const int8_t *qw,
                                      const float *sw, const uint16_t *bias, int64_t M, int64_t N,
                                      int64_t K, uint16_t *y, hipStream_t stream) {
-    Problem p{qx, sx, qw, sw, bias, y, nullptr, N, K, 0, M, 0, N, 0, 0};
-    return launch<false>(p, stream);
+    Problem p{N, K, 0, M, 0, N, 0, 0};
+    return launch<false>(qx, sx, qw, sw, bias, y, nullptr, p, stream);
 }
 
 hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N,
@@ -259,8 +325,8 @@ hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M,
                                   int32_t *partials, hipStream_t stream) {
     (void)M;
     // the partials epilogue reads no scale, bias or output
-    Problem p{qx, nullptr, qw, nullptr, nullptr, nullptr, partials, N, K, m0, m0 + mt, n0, n0 + nt, 0, 0};
-    return launch<true>(p, stream);
+    Problem p{N, K, m0, m0 + mt, n0, n0 + nt, 0, 0};
+    return launch<true>(qx, nullptr, qw, nullptr, nullptr, nullptr, partials, p, stream);
 }
 
 }  // namespace w8a8
