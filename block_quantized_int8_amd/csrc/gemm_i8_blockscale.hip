@@ -168,6 +168,16 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     const int64_t nblk = (n_org + wn * kWaveN) / kBlock;
     const float *sxr = kPartials ? nullptr : sx + mblk * KB;
     const float *swr = kPartials ? nullptr : sw + nblk * KB;
+    // combined scales sx*sw of 64 consecutive K-blocks, one per lane; each
+    // K-block reads its own with readlane (no scalar load, whose lgkmcnt
+    // wait would also drain every LDS read in flight)
+    float sc_lane = 0.0f;
+    auto load_scales = [&](int kb0) {
+        if constexpr (!kPartials) {
+            const int kb = kb0 + lane;
+            sc_lane = kb < KB ? sxr[kb] * swr[kb] : 0.0f;
+        }
+    };
 
     // sub-tile s = 2*i + j: weight rows 32i.., activation rows 32j.. of the wave tile
     f32x16 acc[8];
@@ -187,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) fofs[kk] = frow * kBlock + (swz_slot(frow, kk * 2 + fhalf) << 4);
 
+    load_scales(0);
     issue_loads(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -199,16 +210,20 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
         if (active) {
             const int8_t *xs = lds + stage * kStage + wm * kWaveM * kBlock;
             const int8_t *ws = lds + stage * kStage + kTileM * kBlock + wn * kWaveN * kBlock;
+            // first sub-tile's fragments in MFMA order, then the second
+            // activation fragment set
             i32x4 fx[2][4], fw[2][4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int kk = 0; kk < 4; ++kk) {
+                fw[0][kk] = *reinterpret_cast<const i32x4 *>(ws + fofs[kk]);
+                fx[0][kk] = *reinterpret_cast<const i32x4 *>(xs + fofs[kk]);
+            }
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    fx[j][kk] = *reinterpret_cast<const i32x4 *>(xs + j * 32 * kBlock + fofs[kk]);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) fw[0][kk] = *reinterpret_cast<const i32x4 *>(ws + fofs[kk]);
+            for (int kk = 0; kk < 4; ++kk)
+                fx[1][kk] = *reinterpret_cast<const i32x4 *>(xs + 32 * kBlock + fofs[kk]);
             float scale = 0.0f;
-            if constexpr (!kPartials) scale = sxr[kb] * swr[kb];
+            if constexpr (!kPartials)
+                scale = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lane), kb & 63));
 
             // software pipeline: the MFMAs of sub-tile s run while the VALU
             // dequantizes sub-tile s-1 (for s = 0: the last sub-tile of the
@@ -233,6 +248,16 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
                             dequant_quarter(acc[7], pk[1], prev_scale, kk);
                     }
                 }
+                if constexpr (!kPartials) {
+                    // issue order: MFMA, 8 dequant VALU, MFMA, ...; the next
+                    // weight fragments' LDS reads go right after the first MFMA
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (kk == 0 && j == 0 && i < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    }
+                }
                 if constexpr (kPartials) {
                     const int64_t m = m_org - p.m_begin + wm * kWaveM + j * 32 + frow;
                     const int64_t nt = p.n_end - p.n_begin;
@@ -244,6 +269,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
             }
             prev_scale = scale;
         }
+        if ((kb & 63) == 63 && kb + 1 < KB) load_scales(kb + 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
