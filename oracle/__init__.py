@@ -45,9 +45,11 @@ def lib():
         L.oracle_fp16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_fp16_to_f64.restype = ctypes.c_double
         L.oracle_gelu_bf16.argtypes = [_P, _I64, _P]
+        L.oracle_quantize_rows.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_linear_postscale_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
         for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
                   "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
-                  "oracle_num_threads"):
+                  "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -144,4 +146,31 @@ def gelu_bf16(x_bf16):
     x = _c(x_bf16, np.uint16)
     y = np.empty_like(x)
     _check(lib().oracle_gelu_bf16(_ptr(x), x.size, _ptr(y)), "gelu_bf16")
+    return y
+
+
+def quantize_rows(x_bf16: np.ndarray):
+    """Row-wise INT8 quantization with the 1e-4 floor -> (q int8 [R,C], s fp32 [R])."""
+    x = _c(x_bf16, np.uint16)
+    r, c = x.shape
+    q = np.empty((r, c), np.int8)
+    s = np.empty((r,), np.float32)
+    _check(lib().oracle_quantize_rows(_ptr(x), r, c, _ptr(q), _ptr(s)), "quantize_rows")
+    return q, s
+
+
+def linear_postscale(qx, sx, qw, sw, bias=None, rows=None):
+    """Post-scale output: exact integer sum over K, scales and bias once."""
+    qx = _c(qx, np.int8)
+    qw = _c(qw, np.int8)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    b = None if bias is None else _c(bias, np.uint16)
+    M, K = qx.shape
+    N = qw.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    nr = M if r is None else r.shape[0]
+    y = np.empty((nr, N), np.uint16)
+    _check(lib().oracle_linear_postscale_rows(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(b), M, N, K,
+                                              _ptr(r), nr, _ptr(y)), "linear_postscale")
     return y

@@ -243,6 +243,68 @@ int oracle_linear_bf16_rows(const void *x, int x_dtype, const uint16_t *w, const
     return OR_OK;
 }
 
+/* ------------------------------------------------- post-scale W8A8 variant */
+
+/*
+ * Row-wise INT8 quantization with an epsilon floor (TurboT2VA paper,
+ * architecture-aware inference stack, W8A8 paragraph): for each row i of
+ * x[rows, cols] (an activation row, or an output-channel weight row),
+ * s_i = fl32(max(max_k |x_ik|, eps) / 127) with eps = fl32(1e-4), and
+ * q_ik = clamp(rint(fl32(x_ik / s_i)), -127, 127).  The floor keeps s_i > 0,
+ * so an all-zero row gives q = 0 with s = fl32(eps / 127).
+ */
+int oracle_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int8_t *q, float *s) {
+    if (!x || !q || !s || rows <= 0 || cols <= 0) return OR_ERR_ARG;
+    const float eps = 1e-4f;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float a = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = fabsf(oracle_bf16_to_f32(x[r * cols + c]));
+            if (v > a) a = v;
+        }
+        if (a < eps) a = eps;
+        const float sc = a / 127.0f;
+        s[r] = sc;
+        for (int64_t c = 0; c < cols; ++c) {
+            float t = rintf(oracle_bf16_to_f32(x[r * cols + c]) / sc);
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            q[r * cols + c] = (int8_t)t;
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * Post-scale output: the INT8 products accumulate exactly over the whole of
+ * K, then both scales (and the bias) are applied once:
+ *   Y[m, n] = bf16( (sum_k qx[m, k] * qw[n, k]) * sx[m] * sw[n] (+ bias[n]) ),
+ * exact integer sum (int64 here), fp64 scaling, one rounding to bf16.
+ * Only the listed rows (rows == NULL: all); y is [nrows, N].
+ */
+int oracle_linear_postscale_rows(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                                 const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                 const int64_t *rows, int64_t nrows, uint16_t *y) {
+    if (!qx || !sx || !qw || !sw || !y || M <= 0 || N <= 0 || K <= 0) return OR_ERR_ARG;
+    if (!rows) nrows = M;
+    if (nrows <= 0) return OR_ERR_ARG;
+    for (int64_t t = 0; t < nrows; ++t)
+        if (rows && (rows[t] < 0 || rows[t] >= M)) return OR_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t m = rows ? rows[t] : t;
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) acc += (int64_t)qx[m * K + k] * (int64_t)qw[n * K + k];
+            double v = (double)acc * (double)sx[m] * (double)sw[n];
+            if (bias) v += (double)oracle_bf16_to_f32(bias[n]);
+            y[t * N + n] = oracle_f64_to_bf16(v);
+        }
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------- guard */
 
 /*
