@@ -13,6 +13,10 @@ C entry points:
 * ``debug_kblock_partials(qx, qw, m0, mt, n0, nt)`` -> int32 [mt, nt, K/128]
 * ``W8A8Linear``: a linear layer that quantizes its weight once at
   construction and keeps the bf16 copy for the fallback.
+
+Post-scale form (per-row / per-output-channel scales, scales applied once):
+``quantize_rows``, ``gemm_postscale``, ``linear_postscale`` and
+``W8A8Linear(..., scaling="postscale")``.
 """
 from __future__ import annotations
 
@@ -21,10 +25,12 @@ import ctypes
 import torch
 
 from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP16, DTYPE_FP32, EXPORTS, PATH_BF16, PATH_INT8,
-                   W8A8Error, check, lib)
+                   POSTSCALE_MAX_K, W8A8Error, check, lib)
 
 __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "route",
            "workspace_bytes", "debug_kblock_partials", "W8A8Linear", "W8A8Error", "lib",
+           "quantize_rows", "gemm_postscale", "linear_postscale", "postscale_workspace_bytes",
+           "POSTSCALE_MAX_K",
            "PATH_INT8", "PATH_BF16", "DTYPE_BF16", "DTYPE_FP16", "DTYPE_FP32", "BLOCK", "EXPORTS"]
 
 _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32: DTYPE_FP32}
@@ -109,13 +115,7 @@ def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):
     return out
 
 
-def linear(x, w, qw=None, sw=None, bias=None, out=None, workspace=None):
-    """Guarded W8A8 linear: Y = x @ w.T (+ bias) in bf16; returns (Y, path).
-
-    x may be bf16, fp16 or fp32 with any leading dims (flattened to M rows).
-    The INT8 path needs bf16 x, M, K, N multiples of 128 and (qw, sw);
-    everything else runs the bf16 fallback on ``w``.
-    """
+def _guarded(fn_name, ws_bytes, x, w, qw, sw, bias, out, workspace):
     if not isinstance(x, torch.Tensor) or x.dtype not in _DTYPES:
         raise ValueError("x must be a bf16, fp16 or fp32 tensor")
     _need_cuda("w", w, torch.bfloat16)
@@ -138,15 +138,74 @@ def linear(x, w, qw=None, sw=None, bias=None, out=None, workspace=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need_cuda("out", out, torch.bfloat16)
-    need = workspace_bytes(M, K) if qw is not None else 0
+    need = ws_bytes(M, K) if qw is not None else 0
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     path = ctypes.c_int(-1)
-    check("w8a8_linear",
-          lib().w8a8_linear(_ptr(x2), _DTYPES[x.dtype], M, K, N, _ptr(w), _ptr(qw), _ptr(sw),
-                            _ptr(bias), _ptr(out), _ptr(workspace) if need else None,
-                            need, _stream(x.device), ctypes.byref(path)))
+    check(fn_name,
+          getattr(lib(), fn_name)(_ptr(x2), _DTYPES[x.dtype], M, K, N, _ptr(w), _ptr(qw), _ptr(sw),
+                                  _ptr(bias), _ptr(out), _ptr(workspace) if need else None,
+                                  need, _stream(x.device), ctypes.byref(path)))
     return out.reshape(*lead, N), path.value
+
+
+def linear(x, w, qw=None, sw=None, bias=None, out=None, workspace=None):
+    """Guarded W8A8 linear: Y = x @ w.T (+ bias) in bf16; returns (Y, path).
+
+    x may be bf16, fp16 or fp32 with any leading dims (flattened to M rows).
+    The INT8 path needs bf16 x, M, K, N multiples of 128 and (qw, sw);
+    everything else runs the bf16 fallback on ``w``.
+    """
+    return _guarded("w8a8_linear", workspace_bytes, x, w, qw, sw, bias, out, workspace)
+
+
+def quantize_rows(x: torch.Tensor, q=None, s=None):
+    """Row-wise INT8 quantization with the 1e-4 floor -> (q int8 [R,K], s fp32 [R])."""
+    _need_cuda("x", x, torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = torch.empty((R,), dtype=torch.float32, device=x.device)
+    _need_cuda("q", q, torch.int8)
+    _need_cuda("s", s, torch.float32)
+    if q.numel() != R * C or s.numel() != R:
+        raise ValueError("output buffers have the wrong size")
+    check("w8a8_quantize_rows", lib().w8a8_quantize_rows(_ptr(x), R, C, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def gemm_postscale(qx, sx, qw, sw, bias=None, out=None):
+    """Post-scale INT8 GEMM (int32 over all of K, scales once) -> bf16 [M, N]."""
+    _need_cuda("qx", qx, torch.int8)
+    _need_cuda("qw", qw, torch.int8)
+    _need_cuda("sx", sx, torch.float32)
+    _need_cuda("sw", sw, torch.float32)
+    M, K = qx.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K or sx.numel() != M or sw.numel() != N:
+        raise ValueError("operand shapes disagree")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
+    _need_cuda("out", out, torch.bfloat16)
+    check("w8a8_gemm_postscale",
+          lib().w8a8_gemm_postscale(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(bias), M, N, K,
+                                    _ptr(out), _stream(qx.device)))
+    return out
+
+
+def postscale_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().w8a8_linear_postscale_workspace_bytes(int(M), int(K)))
+
+
+def linear_postscale(x, w, qw=None, sw=None, bias=None, out=None, workspace=None):
+    """Guarded post-scale W8A8 linear (qw, sw from ``quantize_rows``)."""
+    return _guarded("w8a8_linear_postscale", postscale_workspace_bytes, x, w, qw, sw, bias, out,
+                    workspace)
 
 
 def debug_kblock_partials(qx, qw, m0: int, mt: int, n0: int, nt: int):
@@ -165,31 +224,39 @@ def debug_kblock_partials(qx, qw, m0: int, mt: int, n0: int, nt: int):
 class W8A8Linear(torch.nn.Module):
     """Linear layer on the guarded W8A8 path.
 
-    The bf16 weight [N, K] is kept (the fallback needs it) and, when N and K
-    are multiples of 128, quantized once here.  ``forward`` quantizes the
-    activations on every call (or falls back) and returns bf16.
+    The bf16 weight [N, K] is kept (the fallback needs it) and quantized once
+    here: per 128x128 block (``scaling="block"``, the default) or per output
+    channel (``scaling="postscale"``).  ``forward`` quantizes the activations
+    on every call (or falls back) and returns bf16.
     """
 
-    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None):
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, scaling: str = "block"):
         super().__init__()
         _need_cuda("weight", weight, torch.bfloat16)
+        if scaling not in ("block", "postscale"):
+            raise ValueError("scaling is 'block' or 'postscale'")
         self.weight = weight
         self.bias = bias
+        self.scaling = scaling
         N, K = weight.shape
+        self.qweight, self.wscale = None, None
         if N % BLOCK == 0 and K % BLOCK == 0:
-            self.qweight, self.wscale = quantize_weight(weight)
-        else:
-            self.qweight, self.wscale = None, None
+            if scaling == "block":
+                self.qweight, self.wscale = quantize_weight(weight)
+            elif K <= POSTSCALE_MAX_K:
+                self.qweight, self.wscale = quantize_rows(weight)
         self._workspace = None
         self.last_path = None
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         K = self.weight.shape[1]
         M = x.numel() // K if K else 0
-        need = workspace_bytes(M, K) if self.qweight is not None else 0
+        ws_fn = workspace_bytes if self.scaling == "block" else postscale_workspace_bytes
+        need = ws_fn(M, K) if self.qweight is not None else 0
         if need and (self._workspace is None or self._workspace.numel() < need
                      or self._workspace.device != x.device):
             self._workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-        y, self.last_path = linear(x, self.weight, self.qweight, self.wscale, self.bias,
-                                   workspace=self._workspace)
+        fn = linear if self.scaling == "block" else linear_postscale
+        y, self.last_path = fn(x, self.weight, self.qweight, self.wscale, self.bias,
+                               workspace=self._workspace)
         return y

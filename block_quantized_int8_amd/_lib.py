@@ -22,7 +22,10 @@ EXPORTS = (
     "w8a8_quantize_weight", "w8a8_quantize_act", "w8a8_gemm_blockscale",
     "w8a8_linear_workspace_bytes", "w8a8_linear", "w8a8_route",
     "w8a8_debug_kblock_partials", "w8a8_status_string", "w8a8_last_hip_error",
+    "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale_workspace_bytes",
+    "w8a8_linear_postscale",
 )
+POSTSCALE_MAX_K = 133120
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -56,11 +59,17 @@ def lib():
     L.w8a8_route.argtypes = [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int]
     L.w8a8_debug_kblock_partials.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                              _P, _P]
+    L.w8a8_quantize_rows.argtypes = [_P, _I64, _I64, _P, _P, _P]
+    L.w8a8_gemm_postscale.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
+    L.w8a8_linear_postscale_workspace_bytes.argtypes = [_I64, _I64]
+    L.w8a8_linear_postscale_workspace_bytes.restype = ctypes.c_size_t
+    L.w8a8_linear_postscale.argtypes = L.w8a8_linear.argtypes
     L.w8a8_status_string.argtypes = [ctypes.c_int]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
     for f in ("w8a8_quantize_weight", "w8a8_quantize_act", "w8a8_gemm_blockscale", "w8a8_linear",
-              "w8a8_route", "w8a8_debug_kblock_partials", "w8a8_last_hip_error"):
+              "w8a8_route", "w8a8_debug_kblock_partials", "w8a8_last_hip_error",
+              "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

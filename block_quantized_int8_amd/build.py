@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libw8a8.so")
 
-SOURCES = ["w8a8_api.cpp", "quantize_block.hip", "gemm_i8_blockscale.hip", "gemm_bf16.hip"]
+SOURCES = ["w8a8_api.cpp", "quantize_block.hip", "quantize_rows.hip", "gemm_i8_blockscale.hip",
+           "gemm_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -68,6 +68,7 @@ constexpr int kGroupM = 8;
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // buffer descriptor word 3 for raw (untyped) dword buffer access on gfx9 parts
@@ -112,11 +113,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const int8_t *base, 
                                              kRsrcWord3);
 }
 
-template <bool kPartials>
+// kMode: kBlockScaled (the block form), kPartials (test epilogue) or
+// kPostScaled (per-row / per-channel scales applied once at the end).
+enum { kBlockScaled = 0, kPartialsOnly = 1, kPostScaled = 2 };
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     const int8_t *__restrict__ qx, const float *__restrict__ sx, const int8_t *__restrict__ qw,
     const float *__restrict__ sw, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
     int32_t *__restrict__ partials, const Problem p) {
+    constexpr bool kPartials = kMode == kPartialsOnly;
+    constexpr bool kPost = kMode == kPostScaled;
     __shared__ __attribute__((aligned(1024))) int8_t lds[2 * kStage];
 
     // ---- tile index: XCD-contiguous ranges, then grouped m-fastest order
@@ -166,25 +173,33 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     const bool active = (m_org + wm * kWaveM < p.m_end) && (n_org + wn * kWaveN < p.n_end);
     const int64_t mblk = (m_org + wm * kWaveM) / kBlock;
     const int64_t nblk = (n_org + wn * kWaveN) / kBlock;
-    const float *sxr = kPartials ? nullptr : sx + mblk * KB;
-    const float *swr = kPartials ? nullptr : sw + nblk * KB;
+    const float *sxr = kMode == kBlockScaled ? sx + mblk * KB : nullptr;
+    const float *swr = kMode == kBlockScaled ? sw + nblk * KB : nullptr;
     // combined scales sx*sw of 64 consecutive K-blocks, one per lane; each
     // K-block reads its own with readlane (no scalar load, whose lgkmcnt
     // wait would also drain every LDS read in flight)
+    // (only active wavefronts read scales: an inactive one's block row of a
+    // partial edge tile may not exist)
     float sc_lane = 0.0f;
     auto load_scales = [&](int kb0) {
-        if constexpr (!kPartials) {
+        if constexpr (kMode == kBlockScaled) {
             const int kb = kb0 + lane;
-            sc_lane = kb < KB ? sxr[kb] * swr[kb] : 0.0f;
+            sc_lane = (active && kb < KB) ? sxr[kb] * swr[kb] : 0.0f;
         }
     };
 
     // sub-tile s = 2*i + j: weight rows 32i.., activation rows 32j.. of the wave tile
+    // block form: fp32 accumulators; post-scale form: int32 accumulators
+    // carried across all K-blocks by the MFMAs themselves
     f32x16 acc[8];
+    i32x16 acci[kPost ? 8 : 1];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) {
+            acc[s][r] = 0.0f;
+            acci[kPost ? s : 0][r] = 0;
+        }
     i32x16 pk[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) pk[1][r] = 0;
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
             for (int kk = 0; kk < 4; ++kk)
                 fx[1][kk] = *reinterpret_cast<const i32x4 *>(xs + 32 * kBlock + fofs[kk]);
             float scale = 0.0f;
-            if constexpr (!kPartials)
+            if constexpr (kMode == kBlockScaled)
                 scale = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lane), kb & 63));
 
             // software pipeline: the MFMAs of sub-tile s run while the VALU
@@ -236,6 +251,12 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
                     for (int kk = 0; kk < 4; ++kk)
                         fw[(i + 1) & 1][kk] =
                             *reinterpret_cast<const i32x4 *>(ws + (i + 1) * 32 * kBlock + fofs[kk]);
+                }
+                if constexpr (kPost) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        acci[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i & 1][kk], fx[j][kk], acci[s], 0, 0, 0);
+                    continue;
                 }
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -276,8 +297,24 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
 
     if constexpr (!kPartials) {
         if (!active) return;
+        if constexpr (kPost) {
+            // post-scale epilogue: y = float(int32 sum over K) * sx[m] * sw[n]
+            float sxm[2];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) dequant_quarter(acc[7], pk[1], prev_scale, kk);
+            for (int j = 0; j < 2; ++j) sxm[j] = sx[m_org + wm * kWaveM + j * 32 + frow];
+            const float *swp = sw + n_org + wn * kWaveN + fhalf * 4;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(swp + (s >> 1) * 32 + q * 8);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[s][q * 4 + e] = (float)acci[s][q * 4 + e] * sxm[s & 1] * w4[e];
+                }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) dequant_quarter(acc[7], pk[1], prev_scale, kk);
+        }
 
         // ---- epilogue through LDS (free after the last barrier): each wave
         // writes its 64 (m) x 128 (n) bf16 tile as rows of 256 bytes with the
@@ -323,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     }
 }
 
-template <bool kPartials>
+template <int kMode>
 hipError_t launch(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
                   const uint16_t *bias, uint16_t *y, int32_t *partials, Problem p, hipStream_t stream) {
     const int64_t tm = (p.m_end - p.m_begin + kTileM - 1) / kTileM;
@@ -332,7 +369,7 @@ hipError_t launch(const int8_t *qx, const float *sx, const int8_t *qw, const flo
     if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
-    gemm_i8_bs_kernel<kPartials><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+    gemm_i8_bs_kernel<kMode><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
         qx, sx, qw, sw, bias, y, partials, p);
     return hipGetLastError();
 }
@@ -343,7 +380,7 @@ hipError_t launch_gemm_i8_blockscale(const int8_t *qx, const float *sx, const in
                                      const float *sw, const uint16_t *bias, int64_t M, int64_t N,
                                      int64_t K, uint16_t *y, hipStream_t stream) {
     Problem p{N, K, 0, M, 0, N, 0, 0};
-    return launch<false>(qx, sx, qw, sw, bias, y, nullptr, p, stream);
+    return launch<kBlockScaled>(qx, sx, qw, sw, bias, y, nullptr, p, stream);
 }
 
 hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N,
@@ -352,7 +389,14 @@ hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M,
     (void)M;
     // the partials epilogue reads no scale, bias or output
     Problem p{N, K, m0, m0 + mt, n0, n0 + nt, 0, 0};
-    return launch<true>(qx, nullptr, qw, nullptr, nullptr, nullptr, partials, p, stream);
+    return launch<kPartialsOnly>(qx, nullptr, qw, nullptr, nullptr, nullptr, partials, p, stream);
+}
+
+hipError_t launch_gemm_i8_postscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                                    const uint16_t *bias, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                                    hipStream_t stream) {
+    Problem p{N, K, 0, M, 0, N, 0, 0};
+    return launch<kPostScaled>(qx, sx, qw, sw, bias, y, nullptr, p, stream);
 }
 
 }  // namespace w8a8

@@ -140,6 +140,66 @@ int w8a8_debug_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, in
     return hip_status(w8a8::launch_kblock_partials(qx, qw, M, N, K, m0, mt, n0, nt, partials, stream));
 }
 
+int w8a8_quantize_rows(const void *x_bf16, int64_t R, int64_t K, int8_t *q, float *s, hipStream_t stream) {
+    if (!x_bf16 || !q || !s || R <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
+    if (K % 8 || !aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(s, 4)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(q) || !is_device_ptr(s)) return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_quantize_rows(static_cast<const uint16_t *>(x_bf16), R, K, q, s, stream));
+}
+
+int w8a8_gemm_postscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                        const void *bias_bf16, int64_t M, int64_t N, int64_t K, void *y_bf16,
+                        hipStream_t stream) {
+    if (!qx || !sx || !qw || !sw || !y_bf16 || M <= 0 || N <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
+    if (!mult128(M) || !mult128(N) || !mult128(K) || K > W8A8_POSTSCALE_MAX_K) return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(y_bf16, 16) || !aligned(sx, 4) ||
+        !aligned(sw, 16) || !aligned(bias_bf16, 8))
+        return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(qx) || !is_device_ptr(sx) || !is_device_ptr(qw) || !is_device_ptr(sw) ||
+        !is_device_ptr(y_bf16) || (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_gemm_i8_postscale(qx, sx, qw, sw, static_cast<const uint16_t *>(bias_bf16), M,
+                                                     N, K, static_cast<uint16_t *>(y_bf16), stream));
+}
+
+size_t w8a8_linear_postscale_workspace_bytes(int64_t M, int64_t K) {
+    if (!mult128(M) || !mult128(K)) return 0;
+    return round256((size_t)M * (size_t)K) + round256((size_t)M * sizeof(float));
+}
+
+int w8a8_linear_postscale(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
+                          const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out) {
+    if (!x || !w_bf16 || !y_bf16 || M <= 0 || K <= 0 || N <= 0 || !valid_dtype(x_dtype))
+        return W8A8_ERR_INVALID_ARG;
+    if ((qw == nullptr) != (sw == nullptr)) return W8A8_ERR_INVALID_ARG;
+    if (!is_device_ptr(x) || !is_device_ptr(w_bf16) || !is_device_ptr(y_bf16) ||
+        (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+    int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
+    if (path == W8A8_PATH_INT8 && K > W8A8_POSTSCALE_MAX_K) path = W8A8_PATH_BF16;
+    if (path == W8A8_PATH_INT8) {
+        const size_t need = w8a8_linear_postscale_workspace_bytes(M, K);
+        if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
+        if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace)) return W8A8_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || !aligned(y_bf16, 16) || !aligned(qw, 16) || !aligned(workspace, 16) ||
+            !aligned(sw, 16) || !aligned(bias_bf16, 8))
+            path = W8A8_PATH_BF16;
+    }
+    if (path_out) *path_out = path;
+    if (path == W8A8_PATH_INT8) {
+        int8_t *qx = static_cast<int8_t *>(workspace);
+        float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) + round256((size_t)M * (size_t)K));
+        hipError_t e = w8a8::launch_quantize_rows(static_cast<const uint16_t *>(x), M, K, qx, sx, stream);
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(w8a8::launch_gemm_i8_postscale(qx, sx, qw, sw, static_cast<const uint16_t *>(bias_bf16),
+                                                         M, N, K, static_cast<uint16_t *>(y_bf16), stream));
+    }
+    return hip_status(w8a8::launch_gemm_bf16(x, x_dtype, static_cast<const uint16_t *>(w_bf16),
+                                             static_cast<const uint16_t *>(bias_bf16), M, N, K,
+                                             static_cast<uint16_t *>(y_bf16), stream));
+}
+
 const char *w8a8_status_string(int status) {
     switch (status) {
     case W8A8_OK: return "W8A8_OK";

@@ -21,6 +21,13 @@ hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M,
                                   int64_t K, int64_t m0, int64_t mt, int64_t n0, int64_t nt,
                                   int32_t *partials, hipStream_t stream);
 
+// Post-scale form: per-row scales sx[M], per-output-channel scales sw[N].
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int8_t *q, float *s,
+                                hipStream_t stream);
+hipError_t launch_gemm_i8_postscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                                    const uint16_t *bias, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                                    hipStream_t stream);
+
 // x_dtype: 0 bf16, 1 fp16, 2 fp32 (the W8A8_DTYPE_* codes).
 hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
                             int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);

@@ -143,6 +143,53 @@ int w8a8_debug_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, in
                                int64_t m0, int64_t mt, int64_t n0, int64_t nt, int32_t *partials,
                                hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Post-scale form (TurboT2VA paper, architecture-aware inference stack, W8A8
+ * paragraph): static per-output-channel weight scales and dynamic per-row
+ * activation scales, s = max(max-abs, 1e-4) / 127 (eps = fl32(1e-4)), INT32
+ * accumulation over the whole of K, both scales and the bias applied once in
+ * the epilogue.  The guard is the same as for the block form.
+ * ------------------------------------------------------------------------- */
+
+/* Largest K the post-scale GEMM accepts: K * 127^2 must fit in int32. */
+#define W8A8_POSTSCALE_MAX_K 133120
+
+/*
+ * Row-wise quantization: x_bf16 [R, K] -> q int8 [R, K] and s fp32 [R],
+ * s_i = fl32(max(max_k |x_ik|, eps) / 127), q = rint(fl32(x / s)) ties to
+ * even, clamp [-127, 127].  Used for activations (rows = tokens) and weights
+ * (rows = output channels).  Strict: K % 8 != 0 or x/q not 16-byte aligned
+ * -> W8A8_ERR_UNSUPPORTED; null pointers or R, K <= 0 -> W8A8_ERR_INVALID_ARG.
+ */
+int w8a8_quantize_rows(const void *x_bf16, int64_t R, int64_t K, int8_t *q, float *s,
+                       hipStream_t stream);
+
+/*
+ * Post-scale INT8 GEMM:
+ *   Y[m, n] = bf16( float(sum_k qx[m, k] * qw[n, k]) * sx[m] * sw[n] (+ bias[n]) ),
+ * the sum exact in int32 over all K.  qx [M,K], sx [M], qw [N,K], sw [N].
+ * Strict: M, N, K multiples of 128, K <= W8A8_POSTSCALE_MAX_K, qx/qw/y
+ * 16-byte aligned, sw 16-byte aligned, else W8A8_ERR_UNSUPPORTED.
+ */
+int w8a8_gemm_postscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                        const void *bias_bf16, int64_t M, int64_t N, int64_t K, void *y_bf16,
+                        hipStream_t stream);
+
+/* Workspace of w8a8_linear_postscale: qx [M, K] + sx [M], each 256-byte
+ * aligned; 0 when M or K is not a multiple of 128. */
+size_t w8a8_linear_postscale_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * Guarded post-scale linear: same arguments, guard and fallback as
+ * w8a8_linear, with qw/sw from w8a8_quantize_rows (sw [N]).  INT8 path iff
+ * w8a8_route(...) == W8A8_PATH_INT8, K <= W8A8_POSTSCALE_MAX_K and the
+ * pointers are 16-byte aligned; otherwise the bf16 fallback.
+ */
+int w8a8_linear_postscale(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N,
+                          const void *w_bf16, const int8_t *qw, const float *sw,
+                          const void *bias_bf16, void *y_bf16, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream, int *path_out);
+
 /* Static, human-readable name of a W8A8_* status code. */
 const char *w8a8_status_string(int status);
 
