@@ -149,6 +149,12 @@ def gelu_bf16(x_bf16):
     return y
 
 
+def gelu_quantize_block(y_bf16: np.ndarray):
+    """The fused producer's result: GELU rounded to bf16, then the 128x128
+    block quantization of that bf16 matrix -> (q int8, s fp32)."""
+    return quantize_block(gelu_bf16(y_bf16))
+
+
 def quantize_rows(x_bf16: np.ndarray):
     """Row-wise INT8 quantization with the 1e-4 floor -> (q int8 [R,C], s fp32 [R])."""
     x = _c(x_bf16, np.uint16)

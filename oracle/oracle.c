@@ -23,6 +23,11 @@
  *       paragraph; pchao.org summary of TurboT2VA, method overview and
  *       caveats lists.
  *
+ *   - test-harness producer of the MLP-pair workload (not on the pages, which
+ *       leave the MLP's activation open): exact GELU, x * Phi(x) (Hendrycks
+ *       and Gimpel, "Gaussian Error Linear Units"), rounded once to bf16;
+ *       the fused producer's result is that bf16 matrix block-quantized.
+ *
  * Readings taken where the pages are silent (each also listed with the
  * design notes): correctly rounded fp32 division x/s; rint half-to-even;
  * clamp to [-127, 127]; an all-zero block has s = 0 and q = 0 (no epsilon
@@ -324,15 +329,20 @@ int oracle_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight) 
 /* ------------------------------------------------- test-harness producer */
 
 /*
- * Exact-erf GELU in fp64, rounded once to bf16: the producer between the two
- * linears of the MLP-pair workload (not part of the linear layer itself).
+ * Exact GELU, x * Phi(x) with Phi the standard normal CDF, evaluated in fp64
+ * and rounded once to bf16: the producer between the two linears of the
+ * MLP-pair workload (not part of the linear layer itself).  Phi(x) is taken
+ * as erfc(-x / sqrt 2) / 2, which keeps full relative precision for negative
+ * x; the equal form (1 + erf(x / sqrt 2)) / 2 cancels to zero below about
+ * x = -5.5, while the true value stays representable in bf16 down to about
+ * x = -13.5.  Inputs must be finite.
  */
 int oracle_gelu_bf16(const uint16_t *x, int64_t n, uint16_t *y) {
     if (!x || !y || n < 0) return OR_ERR_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         double v = (double)oracle_bf16_to_f32(x[i]);
-        y[i] = oracle_f64_to_bf16(0.5 * v * (1.0 + erf(v / sqrt(2.0))));
+        y[i] = oracle_f64_to_bf16(0.5 * v * erfc(-v / sqrt(2.0)));
     }
     return OR_OK;
 }
