@@ -14,9 +14,15 @@ stream the kernels run on, the roofline of the dominant kernel (the GEMM,
 bound by the INT8 MFMA peak) and the CPU oracle timed on a bounded sample of
 the same workload on this host.
 
-Modes for profiling runs: --only gemm|quantize|linear launches just that
-work for --steps iterations (no oracle); --copy-calibration runs a plain
-1 GiB device copy used to scale the HBM byte counters.
+Also measured (reported beside the headline, not part of a step): the
+post-scale form on the same shape, and the MLP producer fused with the
+quantization (exact GELU + 128x128 block quantize of the MLP's hidden
+activation, 32768 x 16384) against GELU and quantize run one after the other.
+
+Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu
+launches just that work for --steps iterations (no oracle);
+--copy-calibration runs a plain 1 GiB device copy used to scale the HBM byte
+counters.
 """
 from __future__ import annotations
 
@@ -43,7 +49,11 @@ GEMM_BYTES = M * K + N * K + (M // 128 + N // 128) * (K // 128) * 4 + M * N * 2
 GEMM_OPS = 2 * M * N * K
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_i8_attnproj.json")
 GEMM_SOURCE = os.path.join(ROOT, "block_quantized_int8_amd", "csrc", "gemm_i8_blockscale.hip")
-CPU_SAMPLE_BLOCKS = 64      # 128-row blocks of X the oracle processes (8192 of 32768 rows)
+CPU_SAMPLE_BLOCKS = 256     # 128-row blocks of X the oracle processes (all 32768 rows)
+# MLP hidden activation (input of the fused GELU + quantize producer)
+HM, HK = 32768, 16384
+PRODUCER_BYTES = HM * HK * 2 + HM * HK + (HM // 128) * (HK // 128) * 4   # read bf16, write int8 + scales
+GELU_BYTES = HM * HK * 2 * 2                                              # read and write bf16
 
 
 def log(msg):
@@ -108,12 +118,26 @@ def cpu_baseline(d):
                       f"N=K={K}; weight quantization ({t1 - t0:.2f} s) excluded as static"}
 
 
+def producer_buffers(w8a8, dev):
+    """The MLP hidden activation in HBM and the producer's outputs."""
+    import numpy as np
+    import torch
+    from block_quantized_int8_amd.workloads import mlp_hidden
+    t0 = time.perf_counter()
+    yh = torch.from_numpy(mlp_hidden(HM, HK).view(np.int16)).to(dev).view(torch.bfloat16)
+    log(f"MLP hidden activation ready ({time.perf_counter() - t0:.1f} s): {tuple(yh.shape)}")
+    xh = torch.empty_like(yh)
+    qh = torch.empty((HM, HK), dtype=torch.int8, device=dev)
+    sh = torch.empty((HM // 128, HK // 128), dtype=torch.float32, device=dev)
+    return yh, xh, qh, sh
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["gemm", "quantize", "linear"], default=None)
+    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -157,6 +181,16 @@ def main():
     def step():
         _, path = w8a8.linear(x, w, qw, sw, out=y, workspace=ws)
         return path
+
+    if args.only in ("gelu_quant", "gelu"):
+        yh, xh, qh, sh = producer_buffers(w8a8, dev)
+        fn = (lambda: w8a8.gelu_quantize_act(yh, qh, sh)) if args.only == "gelu_quant" else \
+            (lambda: w8a8.gelu_bf16(yh, out=xh))
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"--only {args.only}: {args.steps} launches done")
+        return
 
     if args.only:
         fn = {"linear": step,
@@ -213,7 +247,27 @@ def main():
         qt.append((a, b))
     torch.cuda.synchronize()
     quant_ms = sum(a.elapsed_time(b) for a, b in qt) / args.steps
-    del flush
+
+    # producer A/B on the MLP hidden activation: fused GELU + quantize vs
+    # GELU then quantize, each launch after the same read flush
+    yh, xh, qh, sh = producer_buffers(w8a8, dev)
+    pt = {"fused": [], "gelu": [], "quantize": []}
+    for i in range(args.steps):
+        for key, fn in (("fused", lambda: w8a8.gelu_quantize_act(yh, qh, sh)),
+                        ("gelu", lambda: w8a8.gelu_bf16(yh, out=xh)),
+                        ("quantize", lambda: w8a8.quantize_act(xh, qh, sh))):
+            flush.amax()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            pt[key].append((a, b))
+    torch.cuda.synchronize()
+    prod_us = {k: sum(a.elapsed_time(b) for a, b in v) / args.steps * 1e3 for k, v in pt.items()}
+    del flush, yh, xh, qh, sh
+    log(f"producer A/B (32768x16384): fused {prod_us['fused']:.1f} us "
+        f"({PRODUCER_BYTES / prod_us['fused'] / 1e3:.0f} GB/s) vs gelu {prod_us['gelu']:.1f} + "
+        f"quantize {prod_us['quantize']:.1f} us")
 
     # A/B: the post-scale form (per-row / per-channel scales applied once,
     # INT32 over all of K) on the same inputs and shape
@@ -286,6 +340,16 @@ def main():
                          "gemm_tops": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12, 1),
                          "gemm_frac_of_int8_peak": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                          "quantize_rows_us": round(ps_quant_ms * 1e3, 2)},
+        "producer_ab": {"note": "MLP producer: exact GELU + 128x128 block quantize of the hidden "
+                                "activation, fused vs GELU then quantize (not part of a step)",
+                        "shape": [HM, HK],
+                        "fused_us": round(prod_us["fused"], 2),
+                        "fused_gbs": round(PRODUCER_BYTES / prod_us["fused"] / 1e3, 1),
+                        "fused_frac_of_hbm": round(PRODUCER_BYTES / prod_us["fused"] / 1e3 / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": PRODUCER_BYTES,
+                        "unfused_gelu_us": round(prod_us["gelu"], 2),
+                        "unfused_quantize_us": round(prod_us["quantize"], 2),
+                        "speedup": round((prod_us["gelu"] + prod_us["quantize"]) / prod_us["fused"], 3)},
     }
     print(json.dumps(out), flush=True)
 

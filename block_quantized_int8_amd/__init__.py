@@ -17,6 +17,10 @@ C entry points:
 Post-scale form (per-row / per-output-channel scales, scales applied once):
 ``quantize_rows``, ``gemm_postscale``, ``linear_postscale`` and
 ``W8A8Linear(..., scaling="postscale")``.
+
+Producer fused with the quantization: ``gelu_bf16(x)`` (exact GELU, bf16 in
+and out), ``gelu_quantize_act(y)`` (block quantization of bf16(GELU(y))
+without writing it) and ``W8A8Linear.forward_gelu(y)`` = layer(GELU(y)).
 """
 from __future__ import annotations
 
@@ -30,7 +34,7 @@ from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP16, DTYPE_FP32, EXPORTS, PATH_BF16
 __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "route",
            "workspace_bytes", "debug_kblock_partials", "W8A8Linear", "W8A8Error", "lib",
            "quantize_rows", "gemm_postscale", "linear_postscale", "postscale_workspace_bytes",
-           "POSTSCALE_MAX_K",
+           "POSTSCALE_MAX_K", "gelu_bf16", "gelu_quantize_act",
            "PATH_INT8", "PATH_BF16", "DTYPE_BF16", "DTYPE_FP16", "DTYPE_FP32", "BLOCK", "EXPORTS"]
 
 _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32: DTYPE_FP32}
@@ -92,6 +96,25 @@ def quantize_act(x: torch.Tensor, q=None, s=None):
     """Dynamic 128x128 block INT8 quantization of bf16 activations [M, K]
     (into ``q``/``s`` when given)."""
     return _quantize(lib().w8a8_quantize_act, "x", x, q, s)
+
+
+def gelu_bf16(x: torch.Tensor, out=None):
+    """Exact GELU, x * Phi(x), of a bf16 tensor of any shape, rounded once
+    to bf16 (``out`` may be ``x`` itself)."""
+    _need_cuda("x", x, torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(x)
+    _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
+    check("w8a8_gelu_bf16", lib().w8a8_gelu_bf16(_ptr(x), x.numel(), _ptr(out), _stream(x.device)))
+    return out
+
+
+def gelu_quantize_act(y: torch.Tensor, q=None, s=None):
+    """Block quantization of bf16(GELU(y)) for bf16 y [M, K], fused: the
+    GELU result is never written -> (q int8 [M, K], s fp32 [M/128, K/128])."""
+    return _quantize(lib().w8a8_gelu_quantize_act, "y", y, q, s)
 
 
 def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):
@@ -260,3 +283,28 @@ class W8A8Linear(torch.nn.Module):
         y, self.last_path = fn(x, self.weight, self.qweight, self.wscale, self.bias,
                                workspace=self._workspace)
         return y
+
+    def forward_gelu(self, y: torch.Tensor) -> torch.Tensor:
+        """``self(GELU(y))`` for a bf16 ``y`` [..., K]: the second linear of an
+        MLP with the activation fused into its input quantization when the
+        INT8 block path applies; otherwise GELU runs alone and ``forward``
+        takes its own guarded path."""
+        N, K = self.weight.shape
+        _need_cuda("y", y, torch.bfloat16)
+        if y.shape[-1] != K:
+            raise ValueError(f"last dimension of y must be {K}")
+        M = y.numel() // K
+        fused = (self.scaling == "block" and self.qweight is not None and M > 0
+                 and route(torch.bfloat16, M, K, N, True) == PATH_INT8 and y.data_ptr() % 16 == 0)
+        if not fused:
+            return self.forward(gelu_bf16(y))
+        need = workspace_bytes(M, K)
+        if self._workspace is None or self._workspace.numel() < need or self._workspace.device != y.device:
+            self._workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+        s_off = (M * K + 255) // 256 * 256
+        q = self._workspace[:M * K].view(torch.int8).view(M, K)
+        s = self._workspace[s_off:s_off + 4 * (M // BLOCK) * (K // BLOCK)].view(torch.float32)
+        gelu_quantize_act(y.reshape(M, K), q, s.view(M // BLOCK, K // BLOCK))
+        out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
+        self.last_path = PATH_INT8
+        return out.view(*y.shape[:-1], N)

@@ -23,9 +23,10 @@ EXPORTS = (
     "w8a8_linear_workspace_bytes", "w8a8_linear", "w8a8_route",
     "w8a8_debug_kblock_partials", "w8a8_status_string", "w8a8_last_hip_error",
     "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale_workspace_bytes",
-    "w8a8_linear_postscale",
+    "w8a8_linear_postscale", "w8a8_gelu_bf16", "w8a8_gelu_quantize_act",
 )
 POSTSCALE_MAX_K = 133120
+GELU_QUANT_MAX_K = 8388480
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -64,12 +65,15 @@ def lib():
     L.w8a8_linear_postscale_workspace_bytes.argtypes = [_I64, _I64]
     L.w8a8_linear_postscale_workspace_bytes.restype = ctypes.c_size_t
     L.w8a8_linear_postscale.argtypes = L.w8a8_linear.argtypes
+    L.w8a8_gelu_bf16.argtypes = [_P, _I64, _P, _P]
+    L.w8a8_gelu_quantize_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
     L.w8a8_status_string.argtypes = [ctypes.c_int]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
     for f in ("w8a8_quantize_weight", "w8a8_quantize_act", "w8a8_gemm_blockscale", "w8a8_linear",
               "w8a8_route", "w8a8_debug_kblock_partials", "w8a8_last_hip_error",
-              "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale"):
+              "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale",
+              "w8a8_gelu_bf16", "w8a8_gelu_quantize_act"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

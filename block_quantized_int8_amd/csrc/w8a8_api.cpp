@@ -200,6 +200,26 @@ int w8a8_linear_postscale(const void *x, int x_dtype, int64_t M, int64_t K, int6
                                              static_cast<uint16_t *>(y_bf16), stream));
 }
 
+int w8a8_gelu_bf16(const void *x_bf16, int64_t n, void *y_bf16, hipStream_t stream) {
+    if (n < 0) return W8A8_ERR_INVALID_ARG;
+    if (n == 0) return W8A8_OK;
+    if (!x_bf16 || !y_bf16) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(x_bf16, 2) || !aligned(y_bf16, 2)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(y_bf16)) return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_gelu_bf16(static_cast<const uint16_t *>(x_bf16), n,
+                                             static_cast<uint16_t *>(y_bf16), stream));
+}
+
+int w8a8_gelu_quantize_act(const void *y_bf16, int64_t M, int64_t K, int8_t *qx, float *sx,
+                           hipStream_t stream) {
+    if (!y_bf16 || !qx || !sx || M <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
+    if (!mult128(M) || !mult128(K) || K > W8A8_GELU_QUANT_MAX_K) return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(y_bf16, 16) || !aligned(qx, 16) || !aligned(sx, 4)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(y_bf16) || !is_device_ptr(qx) || !is_device_ptr(sx)) return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_gelu_quantize_block(static_cast<const uint16_t *>(y_bf16), M, K, qx, sx,
+                                                       stream));
+}
+
 const char *w8a8_status_string(int status) {
     switch (status) {
     case W8A8_OK: return "W8A8_OK";

@@ -28,6 +28,11 @@ hipError_t launch_gemm_i8_postscale(const int8_t *qx, const float *sx, const int
                                     const uint16_t *bias, int64_t M, int64_t N, int64_t K, uint16_t *y,
                                     hipStream_t stream);
 
+// Exact GELU (bf16 -> bf16), alone and fused with the 128x128 block quantization.
+hipError_t launch_gelu_bf16(const uint16_t *x, int64_t n, uint16_t *y, hipStream_t stream);
+hipError_t launch_gelu_quantize_block(const uint16_t *y, int64_t rows, int64_t cols, int8_t *q, float *s,
+                                      hipStream_t stream);
+
 // x_dtype: 0 bf16, 1 fp16, 2 fp32 (the W8A8_DTYPE_* codes).
 hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
                             int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);

@@ -16,6 +16,9 @@ these transformer-linear shapes stand in for them:
 * ``c4``  MLP pair: up 32768x16384x4096, then down 32768x4096x16384, seed 3
 * ``c5``  two-stream step: A 65536x4096x4096 (INT8 path) and B 1000x2048x2048
           (guarded to the bf16 fallback), 0.5% outlier channels x30, seed 4
+* ``mlp_hidden``  stand-in for the MLP pair's up-projection output (the input
+          of the fused GELU + quantize producer), 32768 x 16384, seed 5:
+          N(0, 1.28^2), the spread of c4's up projection (sqrt(4096) * 0.02)
 
 Recipe: ``numpy.random.default_rng(seed)`` (PCG64); every tensor is drawn
 with ``standard_normal(shape, dtype=float32)`` in the order listed per config;
@@ -124,3 +127,14 @@ def sample_rows(seed: int, m: int, extra: int = 1024, block: int = 128) -> np.nd
     rng = np.random.default_rng(seed)
     rows.extend(rng.integers(0, m, size=extra).tolist())
     return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def mlp_hidden(m: int = 32768, n: int = 16384, seed: int = 5) -> np.ndarray:
+    """bf16 [m, n] ~ N(0, 1.28^2): the MLP's hidden pre-activation (``m`` or
+    ``n`` may be lowered only by callers that state so)."""
+    rng = np.random.default_rng(seed)
+    a = _normal(rng, (m, n), 1.28)
+    out = np.empty((m, n), np.uint16)
+    for r in range(0, m, 2048):  # bounded temporaries; same bits as one call
+        out[r:r + 2048] = f32_to_bf16_bits(a[r:r + 2048])
+    return out

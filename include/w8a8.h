@@ -190,6 +190,38 @@ int w8a8_linear_postscale(const void *x, int x_dtype, int64_t M, int64_t K, int6
                           const void *bias_bf16, void *y_bf16, void *workspace,
                           size_t workspace_bytes, hipStream_t stream, int *path_out);
 
+/* ---------------------------------------------------------------------------
+ * Producer fused with the activation quantization (TurboT2VA paper,
+ * architecture-aware inference stack: memory-bound elementwise work is fused
+ * into neighbouring kernels).  The producer here is the MLP's activation
+ * between its two linears: exact GELU, x * Phi(x) with Phi the standard
+ * normal CDF (Hendrycks and Gimpel), rounded once to bf16 (nearest, ties to
+ * even).  Results equal an fp64 evaluation of x * erfc(-x / sqrt 2) / 2
+ * rounded once to bf16, for every finite bf16 x.  Inputs must be finite.
+ * ------------------------------------------------------------------------- */
+
+/* Largest K of w8a8_gelu_quantize_act (a 128-row tile must span < 2^31 bytes). */
+#define W8A8_GELU_QUANT_MAX_K 8388480
+
+/*
+ * Elementwise GELU: y[i] = bf16(GELU(x[i])) for i < n (bf16 in, bf16 out).
+ * Any n >= 0 (n = 0 enqueues nothing and accepts null pointers); y may equal
+ * x (in place).  Pointers must be 2-byte aligned device memory, else
+ * W8A8_ERR_UNSUPPORTED / W8A8_ERR_INVALID_ARG; n < 0 -> W8A8_ERR_INVALID_ARG.
+ */
+int w8a8_gelu_bf16(const void *x_bf16, int64_t n, void *y_bf16, hipStream_t stream);
+
+/*
+ * Fused producer + quantize: X' = bf16(GELU(y)) elementwise on y_bf16 [M, K],
+ * then X' is quantized by the block rule of w8a8_quantize_act into qx int8
+ * [M, K] and sx fp32 [M/128, K/128].  X' itself is never written: the codes
+ * and scales equal w8a8_quantize_act applied to w8a8_gelu_bf16(y), bit for
+ * bit.  Strict like w8a8_quantize_act (M, K multiples of 128, y and qx
+ * 16-byte aligned, else W8A8_ERR_UNSUPPORTED), and K <= W8A8_GELU_QUANT_MAX_K.
+ */
+int w8a8_gelu_quantize_act(const void *y_bf16, int64_t M, int64_t K, int8_t *qx, float *sx,
+                           hipStream_t stream);
+
 /* Static, human-readable name of a W8A8_* status code. */
 const char *w8a8_status_string(int status);
 
