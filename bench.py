@@ -248,6 +248,34 @@ def main():
     torch.cuda.synchronize()
     quant_ms = sum(a.elapsed_time(b) for a, b in qt) / args.steps
 
+    # shared-input projections: Q, K, V (3 x 4096 output channels) on X as
+    # three guarded linears vs one group over the concatenated channels
+    import numpy as np
+    from block_quantized_int8_amd.workloads import random_bf16
+    wk = torch.from_numpy(random_bf16(51, (N, K), 0.02).view(np.int16)).to(dev).view(torch.bfloat16)
+    wv = torch.from_numpy(random_bf16(52, (N, K), 0.02).view(np.int16)).to(dev).view(torch.bfloat16)
+    projs = [layer, w8a8.W8A8Linear(wk), w8a8.W8A8Linear(wv)]
+    group = w8a8.W8A8ProjectionGroup([w, wk, wv])
+    group(x)
+    for p in projs:
+        p(x)
+    torch.cuda.synchronize()
+    ga, gb, sa, sb = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    ga.record()
+    for _ in range(args.steps):
+        group(x)
+    gb.record()
+    sa.record()
+    for _ in range(args.steps):
+        for p in projs:
+            p(x)
+    sb.record()
+    torch.cuda.synchronize()
+    qkv_group_us = ga.elapsed_time(gb) / args.steps * 1e3
+    qkv_sep_us = sa.elapsed_time(sb) / args.steps * 1e3
+    del group, projs, wk, wv
+    log(f"QKV 32768x(3x4096)x4096: one group {qkv_group_us:.1f} us vs three linears {qkv_sep_us:.1f} us")
+
     # producer A/B on the MLP hidden activation: fused GELU + quantize vs
     # GELU then quantize, each launch after the same read flush
     yh, xh, qh, sh = producer_buffers(w8a8, dev)
@@ -340,6 +368,11 @@ def main():
                          "gemm_tops": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12, 1),
                          "gemm_frac_of_int8_peak": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                          "quantize_rows_us": round(ps_quant_ms * 1e3, 2)},
+        "qkv_concat_ab": {"note": "Q, K, V projections of X (3 x 4096 output channels): one "
+                                  "concatenated guarded linear vs three (not part of a step)",
+                          "group_us": round(qkv_group_us, 2), "separate_us": round(qkv_sep_us, 2),
+                          "group_tops": round(3 * GEMM_OPS / (qkv_group_us * 1e-6) / 1e12, 1),
+                          "speedup": round(qkv_sep_us / qkv_group_us, 3)},
         "producer_ab": {"note": "MLP producer: exact GELU + 128x128 block quantize of the hidden "
                                 "activation, fused vs GELU then quantize (not part of a step)",
                         "shape": [HM, HK],

@@ -21,6 +21,10 @@ Post-scale form (per-row / per-output-channel scales, scales applied once):
 Producer fused with the quantization: ``gelu_bf16(x)`` (exact GELU, bf16 in
 and out), ``gelu_quantize_act(y)`` (block quantization of bf16(GELU(y))
 without writing it) and ``W8A8Linear.forward_gelu(y)`` = layer(GELU(y)).
+
+Projections sharing one input (Q/K/V, or cross-attention K/V):
+``W8A8ProjectionGroup`` runs them as one guarded linear over the
+concatenated output channels and returns one view per projection.
 """
 from __future__ import annotations
 
@@ -32,7 +36,8 @@ from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP16, DTYPE_FP32, EXPORTS, PATH_BF16
                    POSTSCALE_MAX_K, W8A8Error, check, lib)
 
 __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "route",
-           "workspace_bytes", "debug_kblock_partials", "W8A8Linear", "W8A8Error", "lib",
+           "workspace_bytes", "debug_kblock_partials", "W8A8Linear", "W8A8ProjectionGroup",
+           "W8A8Error", "lib",
            "quantize_rows", "gemm_postscale", "linear_postscale", "postscale_workspace_bytes",
            "POSTSCALE_MAX_K", "gelu_bf16", "gelu_quantize_act",
            "PATH_INT8", "PATH_BF16", "DTYPE_BF16", "DTYPE_FP16", "DTYPE_FP32", "BLOCK", "EXPORTS"]
@@ -308,3 +313,50 @@ class W8A8Linear(torch.nn.Module):
         out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
         self.last_path = PATH_INT8
         return out.view(*y.shape[:-1], N)
+
+
+class W8A8ProjectionGroup(torch.nn.Module):
+    """Linear projections that share one input, run as a single guarded linear.
+
+    The TurboT2VA paper (architecture-aware inference stack, guard paragraph)
+    concatenates the query, key and value projections of a shared input, and
+    the key and value projections of cross-attention, so that the activation
+    is quantized once and one GEMM runs.  Here the weights [N_i, K] are
+    concatenated along the output channels into one ``W8A8Linear``;
+    ``forward(x)`` returns one bf16 view [..., N_i] per projection into the
+    single output [..., sum N_i] (column slices, row stride sum N_i).
+
+    Guard: the INT8 path additionally needs every N_i to be a multiple of
+    128, so that the concatenated weight's 128x128 blocks (or its output
+    channels, in the post-scale form) are exactly the projections' own and
+    each view equals that projection run alone, bit for bit.  Otherwise the
+    group runs the bf16 fallback on the retained concatenated bf16 weight.
+    """
+
+    def __init__(self, weights, biases=None, scaling: str = "block"):
+        super().__init__()
+        weights = list(weights)
+        if not weights:
+            raise ValueError("at least one projection")
+        for i, w in enumerate(weights):
+            _need_cuda(f"weights[{i}]", w, torch.bfloat16)
+            if w.dim() != 2 or w.shape[1] != weights[0].shape[1]:
+                raise ValueError("every weight is [N_i, K] with one common K")
+        if biases is not None and len(biases) != len(weights):
+            raise ValueError("one bias (or None) per projection")
+        self.splits = [int(w.shape[0]) for w in weights]
+        bias = None
+        if biases is not None and any(b is not None for b in biases):
+            bias = torch.cat([b if b is not None else torch.zeros(n, dtype=torch.bfloat16, device=w.device)
+                              for b, n, w in zip(biases, self.splits, weights)])
+        self.linear = W8A8Linear(torch.cat(weights, 0), bias, scaling=scaling)
+        if any(n % BLOCK for n in self.splits):
+            # blocks would straddle two projections: keep the bf16 path only
+            self.linear.qweight, self.linear.wscale = None, None
+
+    @property
+    def last_path(self):
+        return self.linear.last_path
+
+    def forward(self, x: torch.Tensor):
+        return tuple(torch.split(self.linear(x), self.splits, dim=-1))
