@@ -47,9 +47,11 @@ def lib():
         L.oracle_gelu_bf16.argtypes = [_P, _I64, _P]
         L.oracle_quantize_rows.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_linear_postscale_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
+        L.oracle_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
         for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
                   "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
-                  "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows"):
+                  "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
+                  "oracle_quantize_qk"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -147,6 +149,20 @@ def gelu_bf16(x_bf16):
     y = np.empty_like(x)
     _check(lib().oracle_gelu_bf16(_ptr(x), x.size, _ptr(y)), "gelu_bf16")
     return y
+
+
+def quantize_qk(x_bf16: np.ndarray, B: int, L: int, H: int, D: int, ld: int):
+    """Attention Q or K: x holds B*L rows of ``ld`` bf16 values, element
+    (b, l, h, d) at row b*L + l, column h*D + d -> (q int8 [B, H, L, D],
+    s fp32 [B, H, ceil(L/128)])."""
+    x = _c(x_bf16, np.uint16)
+    if x.size != B * L * ld:
+        raise ValueError("x must hold B*L rows of ld values")
+    nblk = -(-L // 128)
+    q = np.empty((B, H, L, D), np.int8)
+    s = np.empty((B, H, nblk), np.float32)
+    _check(lib().oracle_quantize_qk(_ptr(x), B, L, H, D, ld, _ptr(q), _ptr(s)), "quantize_qk")
+    return q, s
 
 
 def gelu_quantize_block(y_bf16: np.ndarray):

@@ -23,6 +23,9 @@
  *       paragraph; pchao.org summary of TurboT2VA, method overview and
  *       caveats lists.
  *
+ *   - INT8 query/key of the sparse attention, block rule over 128 tokens x
+ *       head dim, rearranged sequence-major -> head-major: TurboT2VA paper,
+ *       same section, sparse-attention paragraph.
  *   - test-harness producer of the MLP-pair workload (not on the pages, which
  *       leave the MLP's activation open): exact GELU, x * Phi(x) (Hendrycks
  *       and Gimpel, "Gaussian Error Linear Units"), rounded once to bf16;
@@ -306,6 +309,54 @@ int oracle_linear_postscale_rows(const int8_t *qx, const float *sx, const int8_t
             if (bias) v += (double)oracle_bf16_to_f32(bias[n]);
             y[t * N + n] = oracle_f64_to_bf16(v);
         }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------ attention Q/K, INT8 */
+
+/*
+ * INT8 block quantization of an attention query or key tensor together with
+ * the change from sequence-major to head-major layout (TurboT2VA paper,
+ * architecture-aware inference stack, sparse-attention paragraph: the
+ * adapter rearranges query, key and value into the sparse kernel's layout,
+ * and query and key are quantized to INT8).  Input element (b, l, h, d) is
+ * x[(b * L + l) * ld + h * D + d] (ld >= H * D, the row stride).  Each
+ * (b, h) is cut into blocks of 128 consecutive tokens (the last one may be
+ * shorter); per block a = max |x| over its tokens and all D dims (exact),
+ * s = fl32(a / 127), q = clamp(rint(fl32(x / s)), -127, 127), or s = 0 and
+ * q = 0 when a = 0: the block rule of oracle_quantize_block, taken over
+ * tokens x head dims.  q is int8 [B, H, L, D], s is fp32 [B, H, ceil(L/128)].
+ */
+int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                       int8_t *q, float *s) {
+    if (!x || !q || !s || B <= 0 || L <= 0 || H <= 0 || D <= 0 || ld < H * D) return OR_ERR_ARG;
+    const int64_t nblk = (L + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t task = 0; task < B * H * nblk; ++task) {
+        const int64_t bh = task / nblk, j = task % nblk;
+        const int64_t b = bh / H, h = bh % H;
+        const int64_t l0 = j * ORACLE_BLOCK;
+        const int64_t l1 = l0 + ORACLE_BLOCK < L ? l0 + ORACLE_BLOCK : L;
+        float a = 0.0f;
+        for (int64_t l = l0; l < l1; ++l)
+            for (int64_t d = 0; d < D; ++d) {
+                float v = fabsf(oracle_bf16_to_f32(x[(b * L + l) * ld + h * D + d]));
+                if (v > a) a = v;
+            }
+        const float sc = a / 127.0f;
+        s[bh * nblk + j] = sc;
+        for (int64_t l = l0; l < l1; ++l)
+            for (int64_t d = 0; d < D; ++d) {
+                int8_t out = 0;
+                if (a != 0.0f) {
+                    float t = rintf(oracle_bf16_to_f32(x[(b * L + l) * ld + h * D + d]) / sc);
+                    if (t > 127.0f) t = 127.0f;
+                    if (t < -127.0f) t = -127.0f;
+                    out = (int8_t)t;
+                }
+                q[(bh * L + l) * D + d] = out;
+            }
     }
     return OR_OK;
 }
