@@ -15,11 +15,14 @@ bound by the INT8 MFMA peak) and the CPU oracle timed on a bounded sample of
 the same workload on this host.
 
 Also measured (reported beside the headline, not part of a step): the
-post-scale form on the same shape, and the MLP producer fused with the
-quantization (exact GELU + 128x128 block quantize of the MLP's hidden
-activation, 32768 x 16384) against GELU and quantize run one after the other.
+post-scale form on the same shape; Q, K, V as one concatenated linear vs
+three; the MLP producer fused with the quantization (exact GELU + 128x128
+block quantize of the MLP's hidden activation, 32768 x 16384) against GELU
+and quantize run one after the other; and the INT8 quantization of a video
+self-attention's Q and K (28672 tokens x 32 heads x 128, read from a fused
+Q/K/V output) into the head-major layout.
 
-Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu
+Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk
 launches just that work for --steps iterations (no oracle);
 --copy-calibration runs a plain 1 GiB device copy used to scale the HBM byte
 counters.
@@ -54,6 +57,9 @@ CPU_SAMPLE_BLOCKS = 256     # 128-row blocks of X the oracle processes (all 3276
 HM, HK = 32768, 16384
 PRODUCER_BYTES = HM * HK * 2 + HM * HK + (HM // 128) * (HK // 128) * 4   # read bf16, write int8 + scales
 GELU_BYTES = HM * HK * 2 * 2                                              # read and write bf16
+# attention Q or K of one video self-attention: read bf16, write int8 + one scale per 128 tokens x head
+AL, AH, AD = 28672, 32, 128
+QK_BYTES = AL * AH * AD * 3 + AH * (AL // 128) * 4
 
 
 def log(msg):
@@ -118,6 +124,22 @@ def cpu_baseline(d):
                       f"N=K={K}; weight quantization ({t1 - t0:.2f} s) excluded as static"}
 
 
+def qk_buffers(dev):
+    """A fused Q/K/V output [AL, 3 * AH * AD] in HBM holding the video
+    self-attention's Q and K, and the head-major outputs."""
+    import numpy as np
+    import torch
+    from block_quantized_int8_amd.workloads import attention_qk
+    d = attention_qk(AL, AH, AD)
+    qkv = torch.empty((AL, 3 * AH * AD), dtype=torch.bfloat16, device=dev)
+    for i, name in enumerate(("q", "k")):
+        qkv[:, i * AH * AD:(i + 1) * AH * AD] = torch.from_numpy(d[name].view(np.int16)).to(dev).view(torch.bfloat16)
+    qkv[:, 2 * AH * AD:] = 0
+    qq = torch.empty((AH, AL, AD), dtype=torch.int8, device=dev)
+    sq = torch.empty((AH, AL // 128), dtype=torch.float32, device=dev)
+    return qkv, qq, sq
+
+
 def producer_buffers(w8a8, dev):
     """The MLP hidden activation in HBM and the producer's outputs."""
     import numpy as np
@@ -137,7 +159,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu"], default=None)
+    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -181,6 +203,14 @@ def main():
     def step():
         _, path = w8a8.linear(x, w, qw, sw, out=y, workspace=ws)
         return path
+
+    if args.only == "qk":
+        qkv, qq, sq = qk_buffers(dev)
+        for _ in range(args.steps):
+            w8a8.quantize_qk(qkv[:, :AH * AD], AH, qq, sq)
+        torch.cuda.synchronize()
+        log(f"--only qk: {args.steps} launches done")
+        return
 
     if args.only in ("gelu_quant", "gelu"):
         yh, xh, qh, sh = producer_buffers(w8a8, dev)
@@ -276,9 +306,31 @@ def main():
     del group, projs, wk, wv
     log(f"QKV 32768x(3x4096)x4096: one group {qkv_group_us:.1f} us vs three linears {qkv_sep_us:.1f} us")
 
+    # INT8 attention Q and K from the fused Q/K/V output (row stride 3 * 4096)
+    qkv, qq, sq = qk_buffers(dev)
+    w8a8.quantize_qk(qkv[:, :AH * AD], AH, qq, sq)   # untimed first launch (code object load)
+    torch.cuda.synchronize()
+    qk_t = []
+    for i in range(args.steps):
+        for col in (0, AH * AD):
+            flush.amax()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            w8a8.quantize_qk(qkv[:, col:col + AH * AD], AH, qq, sq)
+            b.record()
+            qk_t.append((a, b))
+    torch.cuda.synchronize()
+    qk_us = sum(a.elapsed_time(b) for a, b in qk_t) / len(qk_t) * 1e3
+    del qkv, qq, sq
+    log(f"Q/K INT8 [{AL}, {AH}x{AD}] from a fused QKV output: {qk_us:.1f} us per tensor "
+        f"({QK_BYTES / qk_us / 1e3:.0f} GB/s)")
+
     # producer A/B on the MLP hidden activation: fused GELU + quantize vs
     # GELU then quantize, each launch after the same read flush
     yh, xh, qh, sh = producer_buffers(w8a8, dev)
+    w8a8.gelu_quantize_act(yh, qh, sh)                # untimed first launches
+    w8a8.gelu_bf16(yh, out=xh)
+    torch.cuda.synchronize()
     pt = {"fused": [], "gelu": [], "quantize": []}
     for i in range(args.steps):
         for key, fn in (("fused", lambda: w8a8.gelu_quantize_act(yh, qh, sh)),
@@ -303,6 +355,8 @@ def main():
     qxp = torch.empty((M, K), dtype=torch.int8, device=dev)
     sxp = torch.empty((M,), dtype=torch.float32, device=dev)
     w8a8.quantize_rows(x, qxp, sxp)
+    w8a8.gemm_postscale(qxp, sxp, qwp, swp, out=y)     # untimed first launch
+    torch.cuda.synchronize()
     evp = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         evp[i][0].record()
@@ -373,6 +427,12 @@ def main():
                           "group_us": round(qkv_group_us, 2), "separate_us": round(qkv_sep_us, 2),
                           "group_tops": round(3 * GEMM_OPS / (qkv_group_us * 1e-6) / 1e12, 1),
                           "speedup": round(qkv_sep_us / qkv_group_us, 3)},
+        "qk_quantize": {"note": "INT8 Q or K of a video self-attention, sequence-major rows of a fused "
+                                "Q/K/V output -> head-major codes + per-128-token scales (not part of a step)",
+                        "shape": {"tokens": AL, "heads": AH, "head_dim": AD, "row_stride": 3 * AH * AD},
+                        "us": round(qk_us, 2), "gbs": round(QK_BYTES / qk_us / 1e3, 1),
+                        "frac_of_hbm": round(QK_BYTES / qk_us / 1e3 / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": QK_BYTES},
         "producer_ab": {"note": "MLP producer: exact GELU + 128x128 block quantize of the hidden "
                                 "activation, fused vs GELU then quantize (not part of a step)",
                         "shape": [HM, HK],

@@ -24,7 +24,9 @@ without writing it) and ``W8A8Linear.forward_gelu(y)`` = layer(GELU(y)).
 
 Projections sharing one input (Q/K/V, or cross-attention K/V):
 ``W8A8ProjectionGroup`` runs them as one guarded linear over the
-concatenated output channels and returns one view per projection.
+concatenated output channels and returns one view per projection;
+``quantize_qk(x, heads)`` turns such a Q or K view (sequence-major) into
+head-major INT8 codes with one scale per 128 tokens of each head.
 """
 from __future__ import annotations
 
@@ -39,7 +41,7 @@ __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "rout
            "workspace_bytes", "debug_kblock_partials", "W8A8Linear", "W8A8ProjectionGroup",
            "W8A8Error", "lib",
            "quantize_rows", "gemm_postscale", "linear_postscale", "postscale_workspace_bytes",
-           "POSTSCALE_MAX_K", "gelu_bf16", "gelu_quantize_act",
+           "POSTSCALE_MAX_K", "gelu_bf16", "gelu_quantize_act", "quantize_qk",
            "PATH_INT8", "PATH_BF16", "DTYPE_BF16", "DTYPE_FP16", "DTYPE_FP32", "BLOCK", "EXPORTS"]
 
 _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32: DTYPE_FP32}
@@ -120,6 +122,36 @@ def gelu_quantize_act(y: torch.Tensor, q=None, s=None):
     """Block quantization of bf16(GELU(y)) for bf16 y [M, K], fused: the
     GELU result is never written -> (q int8 [M, K], s fp32 [M/128, K/128])."""
     return _quantize(lib().w8a8_gelu_quantize_act, "y", y, q, s)
+
+
+def quantize_qk(x: torch.Tensor, heads: int, q=None, s=None):
+    """INT8 attention Q or K: ``x`` is bf16 [B, L, H*D] or [L, H*D],
+    sequence-major, with unit stride in the last dimension (a column slice
+    of a wider row is fine) -> (q int8 [B, H, L, D], s fp32 [B, H, ceil(L/128)]),
+    one scale per block of 128 tokens of each head (H = ``heads``)."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a bf16 CUDA (HIP) tensor")
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    if x3.dim() != 3:
+        raise ValueError("x must be [B, L, H*D] or [L, H*D]")
+    B, L, HD = x3.shape
+    if HD % heads:
+        raise ValueError("the last dimension must be heads * D")
+    D, ld = HD // heads, x3.stride(1)
+    if x3.stride(2) != 1 or (B > 1 and x3.stride(0) != L * ld):
+        raise ValueError("rows of x must be evenly strided with unit-stride columns")
+    nblk = -(-L // BLOCK)
+    if q is None:
+        q = torch.empty((B, heads, L, D), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = torch.empty((B, heads, nblk), dtype=torch.float32, device=x.device)
+    _need_cuda("q", q, torch.int8)
+    _need_cuda("s", s, torch.float32)
+    if q.numel() != B * heads * L * D or s.numel() != B * heads * nblk:
+        raise ValueError("output buffers have the wrong size")
+    check("w8a8_quantize_qk", lib().w8a8_quantize_qk(_ptr(x3), B, L, heads, D, ld, _ptr(q), _ptr(s),
+                                                     _stream(x.device)))
+    return (q, s) if x.dim() == 3 else (q[0], s[0])
 
 
 def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):

@@ -23,7 +23,7 @@ EXPORTS = (
     "w8a8_linear_workspace_bytes", "w8a8_linear", "w8a8_route",
     "w8a8_debug_kblock_partials", "w8a8_status_string", "w8a8_last_hip_error",
     "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale_workspace_bytes",
-    "w8a8_linear_postscale", "w8a8_gelu_bf16", "w8a8_gelu_quantize_act",
+    "w8a8_linear_postscale", "w8a8_gelu_bf16", "w8a8_gelu_quantize_act", "w8a8_quantize_qk",
 )
 POSTSCALE_MAX_K = 133120
 GELU_QUANT_MAX_K = 8388480
@@ -67,13 +67,14 @@ def lib():
     L.w8a8_linear_postscale.argtypes = L.w8a8_linear.argtypes
     L.w8a8_gelu_bf16.argtypes = [_P, _I64, _P, _P]
     L.w8a8_gelu_quantize_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
+    L.w8a8_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.w8a8_status_string.argtypes = [ctypes.c_int]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
     for f in ("w8a8_quantize_weight", "w8a8_quantize_act", "w8a8_gemm_blockscale", "w8a8_linear",
               "w8a8_route", "w8a8_debug_kblock_partials", "w8a8_last_hip_error",
               "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale",
-              "w8a8_gelu_bf16", "w8a8_gelu_quantize_act"):
+              "w8a8_gelu_bf16", "w8a8_gelu_quantize_act", "w8a8_quantize_qk"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

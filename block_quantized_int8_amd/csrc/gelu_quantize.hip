@@ -32,6 +32,7 @@
 // quantizer and gives identical codes and scales for the same bf16 input.
 #include <math.h>
 
+#include "quant_math.h"
 #include "w8a8_internal.h"
 
 namespace w8a8 {
@@ -44,10 +45,7 @@ constexpr int kQuantThreads = 768;
 constexpr int kQuantWaves = kQuantThreads / 64;
 constexpr uint32_t kTableMagLo = 117u << 7;     // |x| = 2^-10
 constexpr uint32_t kTableMagHi = 131u << 7;     // |x| = 16
-constexpr float kRoundMagic = 12582912.0f;      // 1.5 * 2^23
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // fp64 -> bf16 bits, rounded to nearest even, for finite |v| < 2^128.
@@ -132,27 +130,6 @@ __global__ __launch_bounds__(kGeluThreads) void gelu_bf16_kernel(const uint16_t 
 
 constexpr int kTileLoads = 32;  // 16-byte chunks per lane: 128 rows x 16 chunks / 64 lanes
 
-__device__ __forceinline__ uint32_t code_byte(float x, float ss, float r) {
-    const float q0 = x * r;
-    const float e = __builtin_fmaf(-q0, ss, x);
-    const float q1 = __builtin_fmaf(e, r, q0);
-    return __float_as_uint(q1 + kRoundMagic) & 0xFFu;
-}
-
-template <bool kScaled>
-__device__ __forceinline__ uint32_t code_word(uint32_t lo, uint32_t hi, float f, float ss, float r) {
-    float v0 = __uint_as_float(lo << 16), v1 = __uint_as_float(lo & 0xFFFF0000u);
-    float v2 = __uint_as_float(hi << 16), v3 = __uint_as_float(hi & 0xFFFF0000u);
-    if (kScaled) {
-        v0 *= f;
-        v1 *= f;
-        v2 *= f;
-        v3 *= f;
-    }
-    return code_byte(v0, ss, r) | (code_byte(v1, ss, r) << 8) | (code_byte(v2, ss, r) << 16) |
-           (code_byte(v3, ss, r) << 24);
-}
-
 // Buffer descriptors span one tile (rows 128i.., columns 128j..) so that the
 // per-lane offset is 32-bit and each row group's offset is a scalar.
 constexpr int kRsrcFlags = 0x00020000;
@@ -179,14 +156,7 @@ __device__ __forceinline__ void emit_tile_prefetch(u32x4 (&v)[kTileLoads], __amd
     for (int p = 0; p < kTileLoads; ++p) {
         u32x4 w = v[p];
         asm volatile("" : "+v"(w));  // unpack here, chunk by chunk
-        u32x2 c;
-        if (__builtin_expect(scaled, 0)) {
-            c.x = code_word<true>(w.x, w.y, f, ss, r);
-            c.y = code_word<true>(w.z, w.w, f, ss, r);
-        } else {
-            c.x = code_word<false>(w.x, w.y, 1.0f, ss, r);
-            c.y = code_word<false>(w.z, w.w, 1.0f, ss, r);
-        }
+        const u32x2 c = __builtin_expect(scaled, 0) ? code_chunk<true>(w, f, ss, r) : code_chunk<false>(w, 1.0f, ss, r);
         __builtin_amdgcn_raw_buffer_store_b64(c, out, voff, (int)(p * 4 * cols), 0);
         v[p] = __builtin_amdgcn_raw_buffer_load_b128(next, voff * 2, (int)(p * 4 * cols * 2), 0);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads behind their chunk's stores
@@ -195,19 +165,13 @@ __device__ __forceinline__ void emit_tile_prefetch(u32x4 (&v)[kTileLoads], __amd
 
 // Launch requirement (checked by the caller): 128 * cols * 2 bytes < 2^31.
 // Waves own tiles wave, wave + W, wave + 2W, ... (W = waves in the grid).
-// kGelu: quantize GELU(y); otherwise quantize y itself.
-template <bool kGelu>
-__global__ __launch_bounds__(kQuantThreads) void tile_quantize_kernel(const uint16_t *__restrict__ yin,
+__global__ __launch_bounds__(kQuantThreads) void gelu_quantize_kernel(const uint16_t *__restrict__ yin,
                                                                      int64_t cols, int64_t col_blocks,
                                                                      int64_t tiles, int8_t *__restrict__ q,
                                                                      float *__restrict__ s) {
-    const uint16_t *table = nullptr;
-    if constexpr (kGelu) {
-        __shared__ uint16_t lds_table[1 << 16];
-        build_gelu_table(lds_table);
-        __syncthreads();
-        table = lds_table;
-    }
+    __shared__ uint16_t table[1 << 16];
+    build_gelu_table(table);
+    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int r_in = lane >> 4;         // row within each group of 4 rows
     const int c_in = (lane & 15) * 8;   // first of this lane's 8 columns
@@ -232,7 +196,7 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quantize_kernel(const uint
         u16x2 m2 = {0, 0};
 #pragma unroll
         for (int p = 0; p < kTileLoads; ++p) {
-            if constexpr (kGelu) v[p] = gelu_chunk(v[p], table);
+            v[p] = gelu_chunk(v[p], table);
             asm volatile("" : "+v"(v[p]));  // keep only the packed words live
             const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
 #pragma unroll
@@ -248,8 +212,8 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quantize_kernel(const uint
         const float sc = a / 127.0f;  // IEEE division, correctly rounded
         if (lane == 0) s[tile] = sc;
         // an all-zero tile (every value +-0) gets codes 0 from divisor 1
-        const bool scaled = m != 0 && sc < 0x1p-60f;
-        const float f = scaled ? 0x1p64f : 1.0f;
+        const bool scaled = m != 0 && sc < kTinyScale;
+        const float f = scaled ? kPrescale : 1.0f;
         const float ss = m == 0 ? 1.0f : sc * f;
         emit_tile_prefetch(v, tile_rsrc(q + origin_of(tile), span), voff, cols, scaled, f, ss, 1.0f / ss,
                            in_rsrc(tile + step));
@@ -288,7 +252,7 @@ hipError_t launch_gelu_quantize_block(const uint16_t *y, int64_t rows, int64_t c
     if (cus <= 0) return hipErrorInvalidDevice;
     const int64_t need = (tiles + kQuantWaves - 1) / kQuantWaves;
     const unsigned grid = (unsigned)(need < cus ? need : cus);
-    tile_quantize_kernel<true><<<grid, kQuantThreads, 0, stream>>>(y, cols, col_blocks, tiles, q, s);
+    gelu_quantize_kernel<<<grid, kQuantThreads, 0, stream>>>(y, cols, col_blocks, tiles, q, s);
     return hipGetLastError();
 }
 

@@ -14,16 +14,8 @@
 // floats the bit order is the value order), reduced across the wavefront
 // with lane shuffles and across the 4 wavefronts through LDS.
 //
-// Division: with r = fl32(1/s) computed once per block, each element takes
-// q0 = x*r, e = fma(-q0, s, x) (exact remainder), q1 = fma(e, r, q0), which
-// equals the correctly rounded fl32(x/s) (Markstein's correction); it was
-// checked exhaustively against correctly rounded division for every pair of
-// bf16 values 0 < x <= a.  Blocks whose scale is below 2^-60 are first
-// scaled by 2^64 (x and s both, exactly) so that 1/s stays finite and the
-// remainder stays normal.  The ties-to-even rounding to an integer and the
-// int8 conversion are one add: q1 + 1.5*2^23 rounds to the nearest-even
-// integer and its low 8 mantissa bits are q in two's complement (|q1| <= 127,
-// so no clamp is ever active; the a/s <= 127 bound makes that exact).
+// Division and rounding: see quant_math.h.
+#include "quant_math.h"
 #include "w8a8_internal.h"
 
 namespace w8a8 {
@@ -33,43 +25,13 @@ constexpr int kThreads = 256;
 constexpr int kChunksPerRow = kBlock * 2 / 16;                 // 16-byte chunks per block row: 16
 constexpr int kRowsPerPass = kThreads / kChunksPerRow;         // 16
 constexpr int kPasses = kBlock / kRowsPerPass;                 // 8
-constexpr float kRoundMagic = 12582912.0f;                     // 1.5 * 2^23
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t code_byte(float x, float ss, float r) {
-    const float q0 = x * r;
-    const float e = __builtin_fmaf(-q0, ss, x);
-    const float q1 = __builtin_fmaf(e, r, q0);
-    return __float_as_uint(q1 + kRoundMagic) & 0xFFu;
-}
-
-template <bool kScaled>
-__device__ __forceinline__ uint32_t code_word(uint32_t lo_word, uint32_t hi_word, float f, float ss,
-                                              float r) {
-    // lo_word holds elements 0,1 and hi_word elements 2,3 (little endian bf16)
-    float v0 = __uint_as_float(lo_word << 16), v1 = __uint_as_float(lo_word & 0xFFFF0000u);
-    float v2 = __uint_as_float(hi_word << 16), v3 = __uint_as_float(hi_word & 0xFFFF0000u);
-    if (kScaled) {
-        v0 *= f;
-        v1 *= f;
-        v2 *= f;
-        v3 *= f;
-    }
-    return code_byte(v0, ss, r) | (code_byte(v1, ss, r) << 8) | (code_byte(v2, ss, r) << 16) |
-           (code_byte(v3, ss, r) << 24);
-}
 
 template <bool kScaled>
 __device__ __forceinline__ void emit_codes(const u32x4 (&v)[kPasses], int8_t *dst, int64_t cols,
                                            float f, float ss, float r) {
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-        u32x2 out;
-        out.x = code_word<kScaled>(v[p].x, v[p].y, f, ss, r);
-        out.y = code_word<kScaled>(v[p].z, v[p].w, f, ss, r);
-        *reinterpret_cast<u32x2 *>(dst + (int64_t)p * kRowsPerPass * cols) = out;
+        *reinterpret_cast<u32x2 *>(dst + (int64_t)p * kRowsPerPass * cols) = code_chunk<kScaled>(v[p], f, ss, r);
     }
 }
 
@@ -120,8 +82,8 @@ __global__ __launch_bounds__(kThreads) void quantize_block_kernel(const uint16_t
             *reinterpret_cast<u32x2 *>(dst + (int64_t)p * kRowsPerPass * cols) = u32x2{0u, 0u};
         return;
     }
-    if (sc < 0x1p-60f) {
-        const float f = 0x1p64f, ss = sc * f, r = 1.0f / ss;
+    if (sc < kTinyScale) {
+        const float f = kPrescale, ss = sc * f, r = 1.0f / ss;
         emit_codes<true>(v, dst, cols, f, ss, r);
     } else {
         const float r = 1.0f / sc;

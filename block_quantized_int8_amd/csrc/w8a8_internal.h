@@ -33,6 +33,10 @@ hipError_t launch_gelu_bf16(const uint16_t *x, int64_t n, uint16_t *y, hipStream
 hipError_t launch_gelu_quantize_block(const uint16_t *y, int64_t rows, int64_t cols, int8_t *q, float *s,
                                       hipStream_t stream);
 
+// Attention Q/K: sequence-major bf16 -> head-major int8 + per-128-token scales; D is 64 or 128.
+hipError_t launch_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                              int8_t *q, float *s, hipStream_t stream);
+
 // x_dtype: 0 bf16, 1 fp16, 2 fp32 (the W8A8_DTYPE_* codes).
 hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
                             int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);

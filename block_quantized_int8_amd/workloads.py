@@ -16,6 +16,13 @@ these transformer-linear shapes stand in for them:
 * ``c4``  MLP pair: up 32768x16384x4096, then down 32768x4096x16384, seed 3
 * ``c5``  two-stream step: A 65536x4096x4096 (INT8 path) and B 1000x2048x2048
           (guarded to the bf16 fallback), 0.5% outlier channels x30, seed 4
+* ``attention_qk``  query and key of one video self-attention, sequence-major
+          [28672, 32 x 128], seed 6: 28672 = 32 x 56 x 16 latent tokens of a
+          1024x1792, 121-frame clip under 32x32 spatial and 8x temporal
+          compression (assumed; the pages give the resolution and frame count
+          only), 32 heads of 128; N(0, 1.28^2) with 1% of the key's channels
+          x10 (heavy tails); ``l``/``heads``/``d`` select other (e.g. short,
+          ragged audio) sequences
 * ``mlp_hidden``  stand-in for the MLP pair's up-projection output (the input
           of the fused GELU + quantize producer), 32768 x 16384, seed 5:
           N(0, 1.28^2), the spread of c4's up projection (sqrt(4096) * 0.02)
@@ -138,3 +145,13 @@ def mlp_hidden(m: int = 32768, n: int = 16384, seed: int = 5) -> np.ndarray:
     for r in range(0, m, 2048):  # bounded temporaries; same bits as one call
         out[r:r + 2048] = f32_to_bf16_bits(a[r:r + 2048])
     return out
+
+
+def attention_qk(l: int = 28672, heads: int = 32, d: int = 128, seed: int = 6):
+    """{"q", "k"}: bf16 [l, heads * d] each, sequence-major."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (l, heads * d), 1.28)
+    k = _normal(rng, (l, heads * d), 1.28)
+    ch = _outlier_channels(rng, heads * d, 0.01)
+    k[:, ch] *= np.float32(10.0)
+    return {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k)}

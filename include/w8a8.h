@@ -222,6 +222,33 @@ int w8a8_gelu_bf16(const void *x_bf16, int64_t n, void *y_bf16, hipStream_t stre
 int w8a8_gelu_quantize_act(const void *y_bf16, int64_t M, int64_t K, int8_t *qx, float *sx,
                            hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * INT8 query/key for the sparse attention (TurboT2VA paper, architecture-
+ * aware inference stack, sparse-attention paragraph: query and key are
+ * quantized to INT8, and the sequence-major tensors are rearranged into the
+ * attention kernel's layout).  The attention kernel itself is not part of
+ * this library.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * Attention Q or K, quantized per block of 128 tokens x D head dims:
+ *   input  x_bf16, element (b, l, h, d) at x[(b*L + l)*ld + h*D + d]
+ *          (sequence-major; ld >= H*D is the row stride in elements, so x
+ *          may be a column slice of a fused Q/K/V projection output);
+ *   output q int8 [B, H, L, D] (head-major, contiguous) and
+ *          s fp32 [B, H, ceil(L/128)], block j of (b, h) covering tokens
+ *          128j .. min(128j + 127, L - 1);
+ *   rule   the block rule of w8a8_quantize_act over each block's tokens and
+ *          all D dims (s = fl32(max |x| / 127), q = rint(fl32(x / s)) ties
+ *          to even, an all-zero block has s = 0, q = 0).
+ * Any L >= 1 (the last block may be shorter).  D must be 64 or 128, x
+ * 16-byte aligned with ld a multiple of 8, q 16-byte aligned, else
+ * W8A8_ERR_UNSUPPORTED; null pointers, sizes <= 0 or ld < H*D ->
+ * W8A8_ERR_INVALID_ARG.  Inputs must be finite.
+ */
+int w8a8_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, int8_t *q,
+                     float *s, hipStream_t stream);
+
 /* Static, human-readable name of a W8A8_* status code. */
 const char *w8a8_status_string(int status);
 

@@ -95,3 +95,22 @@ def test_host_decided_errors(L):
     # partials window checks
     assert L.w8a8_debug_kblock_partials(fake, fake, 256, 256, 256, 128, 256, 0, 128, fake, null) == 1
     assert L.w8a8_debug_kblock_partials(fake, fake, 256, 256, 256, 64, 128, 0, 128, fake, null) == 2
+
+
+def test_host_decided_errors_producer_and_qk(L):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+    null = None
+    # GELU: negative size; n = 0 is a no-op that accepts null pointers
+    assert L.w8a8_gelu_bf16(fake, -1, fake, null) == 1
+    assert L.w8a8_gelu_bf16(null, 0, null, null) == 0
+    assert L.w8a8_gelu_bf16(ctypes.c_void_p(0x1001), 8, fake, null) == 2
+    # fused GELU + quantize: strict like quantize_act, K bounded
+    assert L.w8a8_gelu_quantize_act(fake, 100, 128, fake, fake, null) == 2
+    assert L.w8a8_gelu_quantize_act(fake, 128, 8388608, fake, fake, null) == 2
+    assert L.w8a8_gelu_quantize_act(null, 128, 128, fake, fake, null) == 1
+    # Q/K: head dim, row stride, alignment
+    assert L.w8a8_quantize_qk(fake, 1, 100, 2, 96, 192, fake, fake, null) == 2
+    assert L.w8a8_quantize_qk(fake, 1, 100, 2, 64, 100, fake, fake, null) == 1
+    assert L.w8a8_quantize_qk(fake, 1, 100, 2, 64, 132, fake, fake, null) == 2
+    assert L.w8a8_quantize_qk(fake, 1, 0, 2, 64, 128, fake, fake, null) == 1
+    assert L.w8a8_quantize_qk(ctypes.c_void_p(0x1008), 1, 100, 2, 64, 128, fake, fake, null) == 2
