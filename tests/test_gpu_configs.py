@@ -113,15 +113,20 @@ def test_mlp_pair():
     d = workloads.c4()
     M = 32768
     y_up, (oqx, osx, oqw_up, osw_up) = _int8_linear_case(d["x"], d["w_up"], 14, "MLP up 32768x16384x4096")
-    # producer between the two linears: exact-erf GELU, computed in fp32, bf16 out
-    xp = torch.nn.functional.gelu(y_up.float()).to(torch.bfloat16)
-    del y_up
+    # producer between the two linears: the library's exact GELU fused into
+    # the down projection's activation quantization
     wd_down = to_dev_bf16(d["w_down"])
-    qw_down, sw_down = w8a8.quantize_weight(wd_down)
+    down = w8a8.W8A8Linear(wd_down)
+    qw_down, sw_down = down.qweight, down.wscale
     oqw_down, osw_down = _check_codes(qw_down, sw_down, d["w_down"], "MLP down weights")
-    y_down, path = w8a8.linear(xp, wd_down, qw_down, sw_down)
+    y_down = down.forward_gelu(y_up)
     torch.cuda.synchronize()
-    assert path == w8a8.PATH_INT8
+    assert down.last_path == w8a8.PATH_INT8
+    # the unfused library chain (GELU written out, then the guarded linear) is bit-identical
+    y_unfused, path = w8a8.linear(w8a8.gelu_bf16(y_up), wd_down, qw_down, sw_down)
+    torch.cuda.synchronize()
+    assert path == w8a8.PATH_INT8 and torch.equal(y_down.view(torch.int16), y_unfused.view(torch.int16))
+    del y_up, y_unfused
     # oracle chain on three 128-row blocks: its own up-projection rows, its
     # own GELU, its own requantization, then the down projection
     blocks = [0, M // 256, M // 128 - 1]
@@ -132,6 +137,9 @@ def test_mlp_pair():
     # the GPU quantizer on the oracle's X' rows: bit-exact requantization
     q2, s2 = w8a8.quantize_act(to_dev_bf16(xo))
     _check_codes(q2, s2, xo, "MLP down requantization of X'")
+    # the fused GELU + quantize on the oracle's up-projection rows: bit-exact too
+    q3, s3 = w8a8.gelu_quantize_act(to_dev_bf16(yo_up))
+    _check_codes(q3, s3, xo, "MLP fused GELU + quantize of the oracle's up-projection rows")
     # the GPU GEMM on those codes vs the oracle's down projection
     yg_blocks = w8a8.gemm_blockscale(q2, s2, qw_down, sw_down)
     yo_down = oracle.linear_int8(oqx2, osx2, oqw_down, osw_down)
