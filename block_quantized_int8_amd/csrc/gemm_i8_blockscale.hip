@@ -267,16 +267,10 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
                             dequant_quarter(acc[s - 1], pk[(s - 1) & 1], scale, kk);
                         else
                             dequant_quarter(acc[7], pk[1], prev_scale, kk);
-                    }
-                }
-                if constexpr (!kPartials) {
-                    // issue order: MFMA, 8 dequant VALU, MFMA, ...; the next
-                    // weight fragments' LDS reads go right after the first MFMA
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        if (kk == 0 && j == 0 && i < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                        // issue order MFMA, its 8 dequant VALU ops, MFMA, ...: a
+                        // hard scheduling fence per pair (group barriers alone
+                        // let the scheduler bunch 4 dependent MFMAs together)
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
                 if constexpr (kPartials) {
