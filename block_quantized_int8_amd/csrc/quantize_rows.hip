@@ -5,51 +5,23 @@
 //   s_i = fl32(max(max_k |x_ik|, eps) / 127),  q_ik = rint(fl32(x_ik / s_i)).
 //
 // One wavefront per row, four rows per workgroup; no LDS and no barrier.
-// Rows of up to 8192 elements stay in registers (each lane holds up to 16
-// chunks of 8 bf16, loaded back to back), so X is read once; longer rows take
-// a second pass over the row for the codes.  The absmax is taken on the
-// magnitude bits and reduced with lane shuffles.  Division and rounding use
-// the same exact scheme as the block quantizer (per-row reciprocal, one FMA
-// correction, ties-to-even by adding 1.5*2^23): the floor keeps s >= 2^-21,
-// and the scheme was checked against correctly rounded division for every
-// bf16 x with the floor's scale as well as for every unfloored one.  |x/s|
-// never exceeds 127, so no clamp is active.
+// Rows of up to 16384 elements stay in registers: each lane holds kChunks
+// chunks of 8 bf16 (the smallest power of two that covers the row, all
+// loaded back to back), so X is read once; longer rows take a second pass
+// over the row for the codes.  The absmax is taken on the magnitude bits and
+// reduced with lane shuffles.  Division and rounding: quant_math.h; the
+// floor keeps s >= 2^-21, far above the range that needs a prescale, and
+// the scheme was checked against correctly rounded division for every bf16
+// x with the floor's scale as well as for every unfloored one.  |x/s| never
+// exceeds 127, so no clamp is active.
+#include "quant_math.h"
 #include "w8a8_internal.h"
 
 namespace w8a8 {
 namespace {
 
 constexpr int kWavesPerGroup = 4;
-constexpr int kMaxChunks = 16;  // per lane: 16 x 8 bf16 -> rows up to 8192 in registers
-constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t code_byte(float x, float s, float r) {
-    const float q0 = x * r;
-    const float e = __builtin_fmaf(-q0, s, x);
-    const float q1 = __builtin_fmaf(e, r, q0);
-    return __float_as_uint(q1 + kRoundMagic) & 0xFFu;
-}
-
-__device__ __forceinline__ u32x2 code_chunk(const u32x4 v, float s, float r) {
-    u32x2 out;
-    out.x = code_byte(__uint_as_float(v.x << 16), s, r) | (code_byte(__uint_as_float(v.x & 0xFFFF0000u), s, r) << 8) |
-            (code_byte(__uint_as_float(v.y << 16), s, r) << 16) |
-            (code_byte(__uint_as_float(v.y & 0xFFFF0000u), s, r) << 24);
-    out.y = code_byte(__uint_as_float(v.z << 16), s, r) | (code_byte(__uint_as_float(v.z & 0xFFFF0000u), s, r) << 8) |
-            (code_byte(__uint_as_float(v.w << 16), s, r) << 16) |
-            (code_byte(__uint_as_float(v.w & 0xFFFF0000u), s, r) << 24);
-    return out;
-}
-
-__device__ __forceinline__ uint32_t mag_max(const u32x4 v) {
-    uint32_t m = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
-    m = max(m, max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-    m = max(m, max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu));
-    return max(m, max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
-}
+constexpr int kMaxChunks = 32;  // per lane: 32 x 8 bf16 -> rows up to 16384 in registers
 
 __device__ __forceinline__ float row_scale(uint32_t m) {
     for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
@@ -57,7 +29,9 @@ __device__ __forceinline__ float row_scale(uint32_t m) {
     return a / 127.0f;  // IEEE division, correctly rounded
 }
 
-template <bool kInRegisters>
+// kChunks > 0: the row in registers, kChunks chunks per lane (kFull: the row
+// is exactly kChunks * 64 chunks, no bounds test); kChunks == 0: two passes.
+template <int kChunks, bool kFull>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void quantize_rows_kernel(const uint16_t *__restrict__ x,
                                                                              int64_t rows, int64_t cols,
                                                                              int8_t *__restrict__ q,
@@ -69,30 +43,39 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void quantize_rows_kernel(cons
     const u32x4 *src = reinterpret_cast<const u32x4 *>(x + row * cols);
     u32x2 *dst = reinterpret_cast<u32x2 *>(q + row * cols);
 
-    if constexpr (kInRegisters) {
-        u32x4 v[kMaxChunks];
+    if constexpr (kChunks > 0) {
+        u32x4 v[kChunks];
         uint32_t m = 0;
 #pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) {
+        for (int c = 0; c < kChunks; ++c) {
             const int64_t ch = (int64_t)c * 64 + lane;
-            v[c] = ch < chunks ? src[ch] : u32x4{0u, 0u, 0u, 0u};
+            v[c] = (kFull || ch < chunks) ? src[ch] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) m = max(m, mag_max(v[c]));
+        for (int c = 0; c < kChunks; ++c) m = max(m, chunk_absmax_bits(v[c]));
         const float sc = row_scale(m), r = 1.0f / sc;
         if (lane == 0) s[row] = sc;
 #pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) {
+        for (int c = 0; c < kChunks; ++c) {
             const int64_t ch = (int64_t)c * 64 + lane;
-            if (ch < chunks) dst[ch] = code_chunk(v[c], sc, r);
+            if (kFull || ch < chunks) dst[ch] = code_chunk<false>(v[c], 1.0f, sc, r);
         }
     } else {
         uint32_t m = 0;
-        for (int64_t ch = lane; ch < chunks; ch += 64) m = max(m, mag_max(src[ch]));
+        for (int64_t ch = lane; ch < chunks; ch += 64) m = max(m, chunk_absmax_bits(src[ch]));
         const float sc = row_scale(m), r = 1.0f / sc;
         if (lane == 0) s[row] = sc;
-        for (int64_t ch = lane; ch < chunks; ch += 64) dst[ch] = code_chunk(src[ch], sc, r);
+        for (int64_t ch = lane; ch < chunks; ch += 64) dst[ch] = code_chunk<false>(src[ch], 1.0f, sc, r);
     }
+}
+
+template <int kChunks>
+void launch_rows(unsigned groups, const uint16_t *x, int64_t rows, int64_t cols, int8_t *q, float *s,
+                 hipStream_t stream) {
+    if (cols / 8 == (int64_t)kChunks * 64)
+        quantize_rows_kernel<kChunks, true><<<groups, 64 * kWavesPerGroup, 0, stream>>>(x, rows, cols, q, s);
+    else
+        quantize_rows_kernel<kChunks, false><<<groups, 64 * kWavesPerGroup, 0, stream>>>(x, rows, cols, q, s);
 }
 
 }  // namespace
@@ -102,10 +85,22 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, i
     const int64_t groups = (rows + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups <= 0) return hipSuccess;
     if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (cols / 8 <= (int64_t)kMaxChunks * 64)
-        quantize_rows_kernel<true><<<dim3((unsigned)groups), dim3(64 * kWavesPerGroup), 0, stream>>>(x, rows, cols, q, s);
+    const unsigned g = (unsigned)groups;
+    const int64_t per_lane = (cols / 8 + 63) / 64;  // chunks per lane
+    if (per_lane <= 1)
+        launch_rows<1>(g, x, rows, cols, q, s, stream);
+    else if (per_lane <= 2)
+        launch_rows<2>(g, x, rows, cols, q, s, stream);
+    else if (per_lane <= 4)
+        launch_rows<4>(g, x, rows, cols, q, s, stream);
+    else if (per_lane <= 8)
+        launch_rows<8>(g, x, rows, cols, q, s, stream);
+    else if (per_lane <= 16)
+        launch_rows<16>(g, x, rows, cols, q, s, stream);
+    else if (per_lane <= kMaxChunks)
+        launch_rows<kMaxChunks>(g, x, rows, cols, q, s, stream);
     else
-        quantize_rows_kernel<false><<<dim3((unsigned)groups), dim3(64 * kWavesPerGroup), 0, stream>>>(x, rows, cols, q, s);
+        quantize_rows_kernel<0, false><<<g, 64 * kWavesPerGroup, 0, stream>>>(x, rows, cols, q, s);
     return hipGetLastError();
 }
 

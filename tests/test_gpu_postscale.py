@@ -28,7 +28,8 @@ def _rows_same(bits, what):
 
 @pytest.mark.parametrize("shape,scale,seed", [((256, 256), 1.0, 1), ((77, 8), 3.0, 2),
                                               ((300, 4096), 0.02, 3), ((64, 8200), 1.0, 4),
-                                              ((40, 16384), 5.0, 5), ((128, 1000), 1e-6, 6)])
+                                              ((40, 16384), 5.0, 5), ((128, 1000), 1e-6, 6),
+                                              ((16, 20008), 2.0, 7), ((200, 4088), 1.0, 8)])
 def test_quantize_rows_random(shape, scale, seed):
     _rows_same(random_bf16(seed, shape, scale), f"rows {shape} x{scale}")
 
