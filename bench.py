@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 M, N, K = 32768, 4096, 4096
 PEAK_INT8_TOPS = 256 * 8192 * 2.4e9 / 1e12   # 5033.2: 256 CUs x 8192 int8 ops/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 2516.6: dense bf16 MFMA
 METRIC = "INT8 GEMM TOPS + % of INT8 MFMA peak; quantize GB/s (M=32768,K=N=4096)"
 # algorithmic bytes of the activation quantization: read bf16 X, write int8
 # qX and one fp32 scale per 128x128 block
@@ -325,6 +326,28 @@ def main():
     log(f"Q/K INT8 [{AL}, {AH}x{AD}] from a fused QKV output: {qk_us:.1f} us per tensor "
         f"({QK_BYTES / qk_us / 1e3:.0f} GB/s)")
 
+    # the guard's bf16 fallback on the shapes that take it: M = 4000 (not a
+    # multiple of 128) at 4096^2, and the two-stream workload's 1000 x 2048^2
+    fb = {}
+    for name, (fm, fn, fk) in (("m4000_n4096_k4096", (4000, 4096, 4096)), ("m1000_n2048_k2048", (1000, 2048, 2048))):
+        xf = torch.from_numpy(random_bf16(70 + fk, (fm, fk)).view(np.int16)).to(dev).view(torch.bfloat16)
+        wf = torch.from_numpy(random_bf16(71 + fk, (fn, fk), 0.02).view(np.int16)).to(dev).view(torch.bfloat16)
+        lf = w8a8.W8A8Linear(wf)
+        lf(xf)
+        torch.cuda.synchronize()
+        assert lf.last_path == w8a8.PATH_BF16
+        fa, fz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fa.record()
+        for _ in range(args.steps):
+            lf(xf)
+        fz.record()
+        torch.cuda.synchronize()
+        us = fa.elapsed_time(fz) / args.steps * 1e3
+        tf = 2 * fm * fn * fk / (us * 1e-6) / 1e12
+        fb[name] = {"us": round(us, 2), "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del xf, wf, lf
+    log("bf16 fallback: " + "; ".join(f"{k} {v['us']} us = {v['tflops']} TFLOP/s" for k, v in fb.items()))
+
     # producer A/B on the MLP hidden activation: fused GELU + quantize vs
     # GELU then quantize, each launch after the same read flush
     yh, xh, qh, sh = producer_buffers(w8a8, dev)
@@ -344,7 +367,7 @@ def main():
             pt[key].append((a, b))
     torch.cuda.synchronize()
     prod_us = {k: sum(a.elapsed_time(b) for a, b in v) / args.steps * 1e3 for k, v in pt.items()}
-    del flush, yh, xh, qh, sh
+    del yh, xh, qh, sh
     log(f"producer A/B (32768x16384): fused {prod_us['fused']:.1f} us "
         f"({PRODUCER_BYTES / prod_us['fused'] / 1e3:.0f} GB/s) vs gelu {prod_us['gelu']:.1f} + "
         f"quantize {prod_us['quantize']:.1f} us")
@@ -357,17 +380,25 @@ def main():
     w8a8.quantize_rows(x, qxp, sxp)
     w8a8.gemm_postscale(qxp, sxp, qwp, swp, out=y)     # untimed first launch
     torch.cuda.synchronize()
-    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
         evp[i][0].record()
-        w8a8.quantize_rows(x, qxp, sxp)
-        evp[i][1].record()
         w8a8.gemm_postscale(qxp, sxp, qwp, swp, out=y)
-        evp[i][2].record()
+        evp[i][1].record()
     torch.cuda.synchronize()
-    ps_quant_ms = sum(e[0].elapsed_time(e[1]) for e in evp) / args.steps
-    ps_gemm_ms = sum(e[1].elapsed_time(e[2]) for e in evp) / args.steps
-    del qxp, qwp
+    ps_gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evp) / args.steps
+    # row quantization timed like the block one: after the same read flush
+    pq = []
+    for i in range(args.steps):
+        flush.amax()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        w8a8.quantize_rows(x, qxp, sxp)
+        b.record()
+        pq.append((a, b))
+    torch.cuda.synchronize()
+    ps_quant_ms = sum(a.elapsed_time(b) for a, b in pq) / args.steps
+    del qxp, qwp, flush
 
     gemm_tops = GEMM_OPS / (gemm_ms * 1e-3) / 1e12
     quant_gbs = QUANT_BYTES / (quant_ms * 1e-3) / 1e9
@@ -422,6 +453,8 @@ def main():
                          "gemm_tops": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12, 1),
                          "gemm_frac_of_int8_peak": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                          "quantize_rows_us": round(ps_quant_ms * 1e3, 2)},
+        "fallback_bf16": {"note": "the guard's bf16 fallback (row-major bf16 MFMA GEMM) on the shapes "
+                                  "that take it; peak = dense bf16 MFMA 2516.6 TFLOP/s", **fb},
         "qkv_concat_ab": {"note": "Q, K, V projections of X (3 x 4096 output channels): one "
                                   "concatenated guarded linear vs three (not part of a step)",
                           "group_us": round(qkv_group_us, 2), "separate_us": round(qkv_sep_us, 2),
