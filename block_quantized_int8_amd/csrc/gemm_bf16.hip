@@ -15,6 +15,12 @@
 // (bf16 input, K % 8 == 0, 16-byte aligned operands); otherwise elements are
 // loaded one by one (per operand: the weight's loads are vectorized
 // whenever K % 8 == 0 and it is 16-byte aligned).
+//
+// This general kernel serves the calls the faster one cannot: bf16 input
+// with K a multiple of 64, N a multiple of 128, 16-byte aligned operands and
+// at least 256 output tiles of 256x256 (any M, e.g. a token count that is
+// not a multiple of 128) goes to the 256x256-tile kernel of the INT8 path in
+// its bf16 mode (launch_gemm_bf16_tiled).
 #include "w8a8_internal.h"
 
 namespace w8a8 {
@@ -186,6 +192,14 @@ hipError_t launch_typed(const void *x, const uint16_t *w, const uint16_t *bias, 
 
 hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
                             int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+    // bf16 input with K a multiple of 64 and N of 128 (any M), large enough to
+    // give every CU a 256x256 tile: the 256x256-tile kernel of the INT8 path in
+    // its bf16 mode (smaller problems keep the 4x more numerous 128x128 tiles)
+    const bool a16 = ((uintptr_t)x % 16 == 0) && ((uintptr_t)w % 16 == 0) && ((uintptr_t)y % 16 == 0);
+    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (x_dtype == 0 && K % 64 == 0 && K <= (1 << 21) && N % 128 == 0 && a16 && (uintptr_t)bias % 8 == 0 &&
+        big_tiles >= 256)
+        return launch_gemm_bf16_tiled(static_cast<const uint16_t *>(x), w, bias, M, N, K, y, stream);
     const bool vec_w = (K % 8 == 0) && ((uintptr_t)w % 16 == 0);
     const bool vec_x = (x_dtype == 0) && vec_w && ((uintptr_t)x % 16 == 0);
     if (vec_x) return launch_typed<0, true, true>(x, w, bias, M, N, K, y, stream);

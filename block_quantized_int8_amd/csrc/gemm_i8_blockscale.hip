@@ -53,6 +53,14 @@
 // main loop) so that Y is written in whole 256-byte row segments.
 //
 // kPartials = true is the test epilogue: the same main loop stores P itself.
+//
+// kBf16 mode runs the guard's bf16 fallback through the same machinery when
+// x is bf16 and K a multiple of 64: a 128-byte LDS row then holds 64 bf16
+// values, and the fragment of v_mfma_f32_32x32x16_bf16 for k-slice kk (lane l:
+// row l%32, elements 16kk + 8(l/32) .. +7) occupies exactly the bytes of the
+// INT8 fragment, so loads, swizzle and fragment reads are unchanged; the
+// MFMAs accumulate straight into the fp32 accumulators (no per-K-block
+// work).  M may be ragged: rows past M read as zeros and are not stored.
 #include "w8a8_internal.h"
 
 namespace w8a8 {
@@ -60,7 +68,6 @@ namespace {
 
 constexpr int kTileM = 256, kTileN = 256;
 constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
 constexpr int kWaveM = 64, kWaveN = 128;
 constexpr int kStage = (kTileM + kTileN) * kBlock;  // bytes per pipeline stage
 constexpr int kGroupM = 8;
@@ -69,6 +76,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // buffer descriptor word 3 for raw (untyped) dword buffer access on gfx9 parts
@@ -79,7 +87,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 // 16 consecutive rows (64 banks, even/odd rows in opposite 128-byte halves)
 // read one chunk column without bank conflicts.  Self-inverse in `chunk`.
 __device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBlock + (swz_slot(row, chunk) << 4); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
@@ -113,9 +120,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const int8_t *base, 
                                              kRsrcWord3);
 }
 
-// kMode: kBlockScaled (the block form), kPartials (test epilogue) or
-// kPostScaled (per-row / per-channel scales applied once at the end).
-enum { kBlockScaled = 0, kPartialsOnly = 1, kPostScaled = 2 };
+// kMode: kBlockScaled (the block form), kPartials (test epilogue),
+// kPostScaled (per-row / per-channel scales applied once at the end) or
+// kBf16 (bf16 operands, fp32 accumulation: the fallback's fast path; the
+// sizes in Problem then count bytes along K).
+enum { kBlockScaled = 0, kPartialsOnly = 1, kPostScaled = 2, kBf16 = 3 };
 
 template <int kMode>
 __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
@@ -124,6 +133,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     int32_t *__restrict__ partials, const Problem p) {
     constexpr bool kPartials = kMode == kPartialsOnly;
     constexpr bool kPost = kMode == kPostScaled;
+    constexpr bool kBf = kMode == kBf16;
     __shared__ __attribute__((aligned(1024))) int8_t lds[2 * kStage];
 
     // ---- tile index: XCD-contiguous ranges, then grouped m-fastest order
@@ -258,6 +268,14 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
                         acci[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i & 1][kk], fx[j][kk], acci[s], 0, 0, 0);
                     continue;
                 }
+                if constexpr (kBf) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fw[i & 1][kk]),
+                                                                         __builtin_bit_cast(bf16x8, fx[j][kk]), acc[s],
+                                                                         0, 0, 0);
+                    continue;
+                }
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     pk[s & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i & 1][kk], fx[j][kk],
@@ -305,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[s][q * 4 + e] = (float)acci[s][q * 4 + e] * sxm[s & 1] * w4[e];
                 }
-        } else {
+        } else if constexpr (!kBf) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) dequant_quarter(acc[7], pk[1], prev_scale, kk);
         }
@@ -345,11 +363,12 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
         __builtin_amdgcn_wave_barrier();
         const int c = lane & 15;
         uint16_t *yrow = y + (m_org + wm * kWaveM) * p.N + n_org + wn * kWaveN + c * 8;
+        const int64_t rows_left = p.m_end - (m_org + wm * kWaveM);  // < 64 only in a ragged last tile
 #pragma unroll
         for (int it = 0; it < kWaveM / 4; ++it) {
             const int row = it * 4 + (lane >> 4);
             const i32x4 v = *reinterpret_cast<const i32x4 *>(ot + row * 256 + ((c ^ (row & 15)) << 4));
-            *reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N) = v;
+            if (row < rows_left) *reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N) = v;
         }
     }
 }
@@ -384,6 +403,14 @@ hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M,
     // the partials epilogue reads no scale, bias or output
     Problem p{N, K, m0, m0 + mt, n0, n0 + nt, 0, 0};
     return launch<kPartialsOnly>(qx, nullptr, qw, nullptr, nullptr, nullptr, partials, p, stream);
+}
+
+hipError_t launch_gemm_bf16_tiled(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M,
+                                  int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+    // K in bytes along the rows: 64 bf16 values per 128-byte K-block
+    Problem p{N, 2 * K, 0, M, 0, N, 0, 0};
+    return launch<kBf16>(reinterpret_cast<const int8_t *>(x), nullptr, reinterpret_cast<const int8_t *>(w),
+                         nullptr, bias, y, nullptr, p, stream);
 }
 
 hipError_t launch_gemm_i8_postscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,

@@ -37,6 +37,11 @@ hipError_t launch_gelu_quantize_block(const uint16_t *y, int64_t rows, int64_t c
 hipError_t launch_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
                               int8_t *q, float *s, hipStream_t stream);
 
+// bf16 fallback on the 256x256-tile kernel: x, w, y 16-byte aligned, K % 64 == 0,
+// K <= 2^21, N % 128 == 0, any M >= 1; bias 8-byte aligned or null.
+hipError_t launch_gemm_bf16_tiled(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M,
+                                  int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+
 // x_dtype: 0 bf16, 1 fp16, 2 fp32 (the W8A8_DTYPE_* codes).
 hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
                             int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);

@@ -119,3 +119,21 @@ def test_repeat_calls_are_deterministic():
     y2 = layer(x)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# bf16 input with K % 64 == 0, N % 128 == 0 and at least 256 output tiles of
+# 256x256 runs the 256x256-tile kernel's bf16 mode: ragged M (a partial last
+# tile, a wavefront half inside it), a partial N tile, 1 to 64 K-blocks of 64
+@pytest.mark.parametrize("M,K,N", [(4000, 64, 4096), (4001, 192, 4224), (8191, 4096, 2048),
+                                   (4100, 128, 4096)])
+def test_fallback_large_tiled(M, K, N):
+    x = random_bf16(M + K + 1, (M, K))
+    w = random_bf16(N + K + 1, (N, K), 0.02)
+    b = random_bf16(N + 1, (N,), 0.1)
+    y, path = w8a8.linear(to_dev_bf16(x), to_dev_bf16(w), bias=to_dev_bf16(b))
+    torch.cuda.synchronize()
+    assert path == w8a8.PATH_BF16
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(M - 200, M),
+                                     np.random.default_rng(M).integers(0, M, 200)]))
+    assert_bf16_close(bf16_bits(y)[rows], oracle.linear_bf16(x, oracle.DTYPE_BF16, w, bias=b, rows=rows),
+                      f"fallback {M}x{K}x{N}")
