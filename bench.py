@@ -18,9 +18,11 @@ Also measured (reported beside the headline, not part of a step): the
 post-scale form on the same shape; Q, K, V as one concatenated linear vs
 three; the MLP producer fused with the quantization (exact GELU + 128x128
 block quantize of the MLP's hidden activation, 32768 x 16384) against GELU
-and quantize run one after the other; and the INT8 quantization of a video
+and quantize run one after the other; the INT8 quantization of a video
 self-attention's Q and K (28672 tokens x 32 heads x 128, read from a fused
-Q/K/V output) into the head-major layout.
+Q/K/V output) into the head-major layout; the guard's bf16 fallback; and a
+two-stream step (an INT8 linear and a guarded-to-bf16 linear launched on
+two streams at once).
 
 Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk
 launches just that work for --steps iterations (no oracle);
@@ -348,6 +350,46 @@ def main():
         del xf, wf, lf
     log("bf16 fallback: " + "; ".join(f"{k} {v['us']} us = {v['tflops']} TFLOP/s" for k, v in fb.items()))
 
+    # two-stream step: A (INT8, 65536 x 4096 x 4096) and B (guarded to the
+    # bf16 fallback, 1000 x 2048 x 2048) launched on two streams at once, and
+    # each alone
+    from block_quantized_int8_amd.workloads import c5
+    d5 = c5()
+    tensor = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    xa5, xb5 = tensor(d5["x_a"]), tensor(d5["x_b"])
+    la5, lb5 = w8a8.W8A8Linear(tensor(d5["w_a"])), w8a8.W8A8Linear(tensor(d5["w_b"]))
+    del d5
+    sa5, sb5 = torch.cuda.Stream(), torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+
+    def two_stream(run_a, run_b):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(cur)
+        for _ in range(args.steps):
+            start = torch.cuda.Event()
+            start.record(cur)
+            ends = []
+            for run, st5, lay, xin in ((run_a, sa5, la5, xa5), (run_b, sb5, lb5, xb5)):
+                if not run:
+                    continue
+                st5.wait_event(start)
+                with torch.cuda.stream(st5):
+                    lay(xin)
+                e = torch.cuda.Event()
+                e.record(st5)
+                ends.append(e)
+            for e in ends:
+                cur.wait_event(e)
+        t1.record(cur)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps * 1e3
+
+    two_stream(True, True)  # untimed first launches
+    assert la5.last_path == w8a8.PATH_INT8 and lb5.last_path == w8a8.PATH_BF16
+    ts_both, ts_a, ts_b = two_stream(True, True), two_stream(True, False), two_stream(False, True)
+    del xa5, xb5, la5, lb5
+    log(f"two-stream step: both {ts_both:.1f} us; A alone {ts_a:.1f} us, B alone {ts_b:.1f} us")
+
     # producer A/B on the MLP hidden activation: fused GELU + quantize vs
     # GELU then quantize, each launch after the same read flush
     yh, xh, qh, sh = producer_buffers(w8a8, dev)
@@ -453,6 +495,9 @@ def main():
                          "gemm_tops": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12, 1),
                          "gemm_frac_of_int8_peak": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                          "quantize_rows_us": round(ps_quant_ms * 1e3, 2)},
+        "two_stream": {"note": "A: INT8 linear 65536x4096x4096 (0.5% channels x30); B: 1000x2048x2048 "
+                               "guarded to the bf16 fallback; launched on two streams per step (not the headline)",
+                       "step_us": round(ts_both, 2), "a_alone_us": round(ts_a, 2), "b_alone_us": round(ts_b, 2)},
         "fallback_bf16": {"note": "the guard's bf16 fallback (row-major bf16 MFMA GEMM) on the shapes "
                                   "that take it; peak = dense bf16 MFMA 2516.6 TFLOP/s", **fb},
         "qkv_concat_ab": {"note": "Q, K, V projections of X (3 x 4096 output channels): one "
