@@ -96,8 +96,8 @@ def ensure_built():
 def make_inputs(dev):
     import numpy as np
     import torch
-    from block_quantized_int8_amd.workloads import c3
-    d = c3(M)
+    from block_quantized_int8_amd.workloads import attention_projection
+    d = attention_projection(M)
     x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
     w = torch.from_numpy(d["w"].view(np.int16)).to(dev).view(torch.bfloat16)
     return d, x, w
@@ -353,8 +353,8 @@ def main():
     # two-stream step: A (INT8, 65536 x 4096 x 4096) and B (guarded to the
     # bf16 fallback, 1000 x 2048 x 2048) launched on two streams at once, and
     # each alone
-    from block_quantized_int8_amd.workloads import c5
-    d5 = c5()
+    from block_quantized_int8_amd.workloads import two_stream
+    d5 = two_stream()
     tensor = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     xa5, xb5 = tensor(d5["x_a"]), tensor(d5["x_b"])
     la5, lb5 = w8a8.W8A8Linear(tensor(d5["w_a"])), w8a8.W8A8Linear(tensor(d5["w_b"]))

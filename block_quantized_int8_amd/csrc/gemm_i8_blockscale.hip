@@ -38,13 +38,16 @@
 //     in groups of 8 m-tiles sweeping n, so tiles resident on one XCD share
 //     operand panels in its L2.
 //
-// Edges: M, N, K are multiples of 128 but not necessarily of 256; rows past
-// the end of a partial tile read as zeros (buffer range check), and
-// wavefronts whose sub-tile lies outside the output skip their work.
+// Edges: N and K are multiples of 128 (K-blocks of 128 bytes), M of 128 in
+// the INT8 modes and arbitrary in the bf16 mode, none necessarily of 256;
+// rows past the end of a partial tile read as zeros (buffer range check),
+// wavefronts whose sub-tile lies outside the output skip their work, and
+// output rows past M are not stored.
 //
 // Within a wavefront the K-block loop is software-pipelined: the four MFMAs
 // of sub-tile s are interleaved with the 32 VALU ops that dequantize the
-// finished partial of sub-tile s-1, so the matrix core and the VALU work at
+// finished partial of sub-tile s-1 (a scheduling fence after every MFMA and
+// its 8 VALU ops holds that order), so the matrix core and the VALU work at
 // the same time.
 //
 // The weight fragment is the MFMA "A" operand and the activation fragment
@@ -52,7 +55,7 @@
 // row m per register group.  The output goes through LDS (free after the
 // main loop) so that Y is written in whole 256-byte row segments.
 //
-// kPartials = true is the test epilogue: the same main loop stores P itself.
+// The partials mode is the test epilogue: the same main loop stores P itself.
 //
 // kBf16 mode runs the guard's bf16 fallback through the same machinery when
 // x is bf16 and K a multiple of 64: a 128-byte LDS row then holds 64 bf16
@@ -101,7 +104,7 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 // in-flight operand prefetch in the same vmcnt queue).
 struct Problem {
     int64_t N, K;
-    int64_t m_begin, m_end, n_begin, n_end;  // output window (multiples of 128)
+    int64_t m_begin, m_end, n_begin, n_end;  // output window (multiples of 128, m_end any in bf16 mode)
     int tiles_m, tiles_n;
 };
 

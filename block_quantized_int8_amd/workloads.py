@@ -9,12 +9,12 @@ The pages give no layer widths or token counts for the video-audio model
 (TurboT2VA paper, experiments: LTX-2 at 1024x1792, 121 frames, batch 1), so
 these transformer-linear shapes stand in for them:
 
-* ``c1``  single linear, M=N=K=256 (2x2 blocks on each operand), seed 0
-* ``c2``  square 4096^3, seed 1, plus a guard case with M=4000 (same W)
-* ``c3``  attention-projection shape M=32768, N=K=4096 with heavy-tailed
+* ``single_linear_256``  M=N=K=256 (2x2 blocks on each operand), seed 0
+* ``square_4096``  square 4096^3, seed 1, plus a guard case with M=4000 (same W)
+* ``attention_projection``  attention-projection shape M=32768, N=K=4096 with heavy-tailed
           activations (1% of K channels scaled by 20), seed 2
-* ``c4``  MLP pair: up 32768x16384x4096, then down 32768x4096x16384, seed 3
-* ``c5``  two-stream step: A 65536x4096x4096 (INT8 path) and B 1000x2048x2048
+* ``mlp_pair``  MLP pair: up 32768x16384x4096, then down 32768x4096x16384, seed 3
+* ``two_stream``  two-stream step: A 65536x4096x4096 (INT8 path) and B 1000x2048x2048
           (guarded to the bf16 fallback), 0.5% outlier channels x30, seed 4
 * ``attention_qk``  query and key of one video self-attention, sequence-major
           [28672, 32 x 128], seed 6: 28672 = 32 x 56 x 16 latent tokens of a
@@ -25,14 +25,14 @@ these transformer-linear shapes stand in for them:
           ragged audio) sequences
 * ``mlp_hidden``  stand-in for the MLP pair's up-projection output (the input
           of the fused GELU + quantize producer), 32768 x 16384, seed 5:
-          N(0, 1.28^2), the spread of c4's up projection (sqrt(4096) * 0.02)
+          N(0, 1.28^2), the spread of the MLP pair's up projection (sqrt(4096) * 0.02)
 
 Recipe: ``numpy.random.default_rng(seed)`` (PCG64); every tensor is drawn
-with ``standard_normal(shape, dtype=float32)`` in the order listed per config;
+with ``standard_normal(shape, dtype=float32)`` in the order listed per workload;
 weights are multiplied by 0.02 and outlier channels by their factor in fp32;
 each fp32 array is converted to bf16 once, round-to-nearest-even on the bits.
 Outlier channels are ``rng.choice(K, round(p*K), replace=False)`` drawn after
-all tensors of the config.
+all tensors of the workload.
 """
 from __future__ import annotations
 
@@ -69,14 +69,14 @@ def _outlier_channels(rng, k: int, frac: float) -> np.ndarray:
     return rng.choice(k, n, replace=False)
 
 
-def c1():
+def single_linear_256():
     rng = np.random.default_rng(0)
     x = _normal(rng, (256, 256))
     w = _normal(rng, (256, 256), WEIGHT_STD)
     return {"x": f32_to_bf16_bits(x), "w": f32_to_bf16_bits(w)}
 
 
-def c2():
+def square_4096():
     rng = np.random.default_rng(1)
     x = _normal(rng, (4096, 4096))
     w = _normal(rng, (4096, 4096), WEIGHT_STD)
@@ -84,8 +84,8 @@ def c2():
     return {"x": f32_to_bf16_bits(x), "w": f32_to_bf16_bits(w), "x_guard": f32_to_bf16_bits(xg)}
 
 
-def c3(m: int = 32768):
-    """Headline shape. ``m`` may be lowered only by callers that state so."""
+def attention_projection(m: int = 32768):
+    """The benchmarked shape. ``m`` may be lowered only by callers that state so."""
     rng = np.random.default_rng(2)
     x = _normal(rng, (m, 4096))
     w = _normal(rng, (4096, 4096), WEIGHT_STD)
@@ -94,7 +94,7 @@ def c3(m: int = 32768):
     return {"x": f32_to_bf16_bits(x), "w": f32_to_bf16_bits(w), "outlier_channels": np.sort(ch)}
 
 
-def c4():
+def mlp_pair():
     rng = np.random.default_rng(3)
     x = _normal(rng, (32768, 4096))
     w_up = _normal(rng, (16384, 4096), WEIGHT_STD)
@@ -103,7 +103,7 @@ def c4():
             "w_down": f32_to_bf16_bits(w_down)}
 
 
-def c5():
+def two_stream():
     rng = np.random.default_rng(4)
     xa = _normal(rng, (65536, 4096))
     wa = _normal(rng, (4096, 4096), WEIGHT_STD)

@@ -6,7 +6,7 @@ import torch
 
 import block_quantized_int8_amd as w8a8
 import oracle
-from block_quantized_int8_amd.workloads import c1, random_bf16
+from block_quantized_int8_amd.workloads import single_linear_256, random_bf16
 from parity import assert_bf16_close, bf16_bits, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -16,8 +16,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def test_partials_c1_full():
-    d = c1()
+def test_partials_single_linear_256_full():
+    d = single_linear_256()
     qx, sx = oracle.quantize_block(d["x"])
     qw, sw = oracle.quantize_block(d["w"])
     p = w8a8.debug_kblock_partials(_dev(qx), _dev(qw), 0, 256, 0, 256)

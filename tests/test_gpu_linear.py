@@ -7,14 +7,14 @@ import torch
 
 import block_quantized_int8_amd as w8a8
 import oracle
-from block_quantized_int8_amd.workloads import c1, random_bf16
+from block_quantized_int8_amd.workloads import single_linear_256, random_bf16
 from parity import assert_bf16_close, bf16_bits, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
 
-def test_c1_linear_int8_path():
-    d = c1()
+def test_single_linear_256_int8_path():
+    d = single_linear_256()
     x, w = to_dev_bf16(d["x"]), to_dev_bf16(d["w"])
     layer = w8a8.W8A8Linear(w)
     y = layer(x)
@@ -24,7 +24,7 @@ def test_c1_linear_int8_path():
     oqw, osw = oracle.quantize_block(d["w"])
     assert np.array_equal(layer.qweight.cpu().numpy(), oqw)
     assert np.array_equal(layer.wscale.cpu().numpy(), osw)
-    assert_bf16_close(bf16_bits(y), oracle.linear_int8(oqx, osx, oqw, osw), "c1")
+    assert_bf16_close(bf16_bits(y), oracle.linear_int8(oqx, osx, oqw, osw), "single linear 256^3")
 
 
 def test_linear_with_bias_and_leading_dims():

@@ -84,7 +84,7 @@ def test_gemm_postscale_extremes():
 
 
 def test_linear_postscale_attention_projection():
-    d = workloads.c3()
+    d = workloads.attention_projection()
     xd, wd = to_dev_bf16(d["x"]), to_dev_bf16(d["w"])
     layer = w8a8.W8A8Linear(wd, scaling="postscale")
     y = layer(xd)

@@ -80,7 +80,7 @@ def test_cross_attention_kv_group_and_guards():
 
 def test_qkv_group_attention_projection_shape():
     # Q, K, V of the attention-projection workload's input: 32768 x 4096 -> 3 x 4096
-    d = workloads.c3()
+    d = workloads.attention_projection()
     wq = d["w"]
     wk = random_bf16(51, (4096, 4096), 0.02)
     wv = random_bf16(52, (4096, 4096), 0.02)

@@ -5,7 +5,7 @@ import torch
 
 import block_quantized_int8_amd as w8a8
 import oracle
-from block_quantized_int8_amd.workloads import c1, f32_to_bf16_bits, random_bf16
+from block_quantized_int8_amd.workloads import single_linear_256, f32_to_bf16_bits, random_bf16
 from conftest import load_golden
 from parity import to_dev_bf16
 
@@ -30,10 +30,10 @@ def _assert_same(bits, weight=False, what=""):
                              f"gpu {q[r, c]} oracle {oq[r, c]} x_bits {bits[r, c]:#06x}")
 
 
-def test_c1_weight_and_activation():
-    d = c1()
-    _assert_same(d["x"], False, "c1 x")
-    _assert_same(d["w"], True, "c1 w")
+def test_single_linear_256_weight_and_activation():
+    d = single_linear_256()
+    _assert_same(d["x"], False, "single linear 256^3: x")
+    _assert_same(d["w"], True, "single linear 256^3: w")
 
 
 @pytest.mark.parametrize("shape,scale,seed", [((384, 640), 1.0, 1), ((128, 128), 3e-3, 2),

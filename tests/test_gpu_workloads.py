@@ -82,14 +82,14 @@ def _int8_linear_case(x_bits, w_bits, seed, what, bias_bits=None):
 
 
 def test_single_linear_256():
-    d = workloads.c1()
+    d = workloads.single_linear_256()
     y, (oqx, osx, oqw, osw) = _int8_linear_case(d["x"], d["w"], 10, "single linear 256^3")
     # small enough for the whole output and all partials
     assert_bf16_close(bf16_bits(y), oracle.linear_int8(oqx, osx, oqw, osw), "single linear, all rows")
 
 
 def test_square_4096_and_guard():
-    d = workloads.c2()
+    d = workloads.square_4096()
     _int8_linear_case(d["x"], d["w"], 11, "square 4096^3")
     # guard case: M = 4000 is not a multiple of 128 -> bf16 fallback
     wd = to_dev_bf16(d["w"])
@@ -105,12 +105,12 @@ def test_square_4096_and_guard():
 
 
 def test_attention_projection_32768():
-    d = workloads.c3()
+    d = workloads.attention_projection()
     _int8_linear_case(d["x"], d["w"], 13, "attention projection 32768x4096x4096")
 
 
 def test_mlp_pair():
-    d = workloads.c4()
+    d = workloads.mlp_pair()
     M = 32768
     y_up, (oqx, osx, oqw_up, osw_up) = _int8_linear_case(d["x"], d["w_up"], 14, "MLP up 32768x16384x4096")
     # producer between the two linears: the library's exact GELU fused into
@@ -150,7 +150,7 @@ def test_mlp_pair():
 
 
 def test_two_stream_step():
-    d = workloads.c5()
+    d = workloads.two_stream()
     xa, wa = to_dev_bf16(d["x_a"]), to_dev_bf16(d["w_a"])
     xb, wb = to_dev_bf16(d["x_b"]), to_dev_bf16(d["w_b"])
     la, lb = w8a8.W8A8Linear(wa), w8a8.W8A8Linear(wb)
