@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -69,20 +70,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def code_sha(path):
+    """Hash of a kernel source's code: comments removed and whitespace
+    collapsed, so that editing comments does not retire measured counters."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
 def load_traffic():
     """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or
-    None when absent or taken on a different version of the kernel source."""
+    None when absent or taken on different kernel code."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(GEMM_SOURCE):
+    if t.get("code_sha") != code_sha(GEMM_SOURCE):
         return None
     return t.get("bytes_per_launch")
 
