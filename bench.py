@@ -109,6 +109,17 @@ def make_inputs(dev):
     return d, x, w
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d):
     """The oracle (untuned) on the first CPU_SAMPLE_BLOCKS row-blocks of X:
     quantize those rows and compute their full output rows."""
@@ -123,12 +134,15 @@ def cpu_baseline(d):
     qw, sw = oracle.quantize_block(d["w"])            # static: excluded below
     t1 = time.perf_counter()
     qx, sx = oracle.quantize_block(xs)
-    oracle.linear_int8(qx, sx, qw, sw)
     t2 = time.perf_counter()
-    secs = t2 - t1
+    oracle.linear_int8(qx, sx, qw, sw)
+    t3 = time.perf_counter()
+    secs = t3 - t1
     ops = 2 * rows * N * K
     return {"value": ops / secs / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(secs, 3),
+            "quantize_seconds": round(t2 - t1, 3), "gemm_seconds": round(t3 - t2, 3),
+            "cpu_model": cpu_model(),
             "sample": f"first {rows} of {M} rows of X (quantize + full output rows), "
                       f"N=K={K}; weight quantization ({t1 - t0:.2f} s) excluded as static"}
 
