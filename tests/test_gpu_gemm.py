@@ -6,7 +6,7 @@ import torch
 
 import block_quantized_int8_amd as w8a8
 import oracle
-from block_quantized_int8_amd.workloads import single_linear_256, random_bf16
+from block_quantized_int8_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits, random_bf16, single_linear_256
 from parity import assert_bf16_close, bf16_bits, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -75,3 +75,19 @@ def test_gemm_zero_rows():
     y = bf16_bits(w8a8.gemm_blockscale(_dev(qx), _dev(sx), _dev(qw), _dev(sw)))
     assert not y[128:].any()
     assert_bf16_close(y, oracle.linear_int8(qx, sx, qw, sw), "zero rows")
+
+
+def test_block_gemm_long_k_scale_reload():
+    # K = 65536: 512 K-blocks, the per-lane scale preload is refilled every 64
+    M = N = 128
+    K = 65536
+    x = random_bf16(91, (M, K))
+    w = random_bf16(92, (N, K), 0.02)
+    # scales vary strongly along K so that a stale or shifted scale shows
+    x = (bf16_bits_to_f32(x).reshape(M, K // 128, 128) * np.float32(2.0) ** (np.arange(K // 128) % 7)[None, :, None])
+    x = f32_to_bf16_bits(x.reshape(M, K))
+    qx, sx = oracle.quantize_block(x)
+    qw, sw = oracle.quantize_block(w)
+    y = w8a8.gemm_blockscale(_dev(qx), _dev(sx), _dev(qw), _dev(sw))
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(y), oracle.linear_int8(qx, sx, qw, sw), "block GEMM K=65536")

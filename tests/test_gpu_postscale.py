@@ -114,3 +114,23 @@ def test_linear_postscale_guard_and_bias():
     qx, sx = oracle.quantize_rows(x[:896])
     qw, sw = oracle.quantize_rows(w)
     assert_bf16_close(bf16_bits(y2), oracle.linear_postscale(qx, sx, qw, sw, bias=b), "post-scale with bias")
+
+
+def test_gemm_postscale_max_k_at_the_int32_limit():
+    # K = 133120 is the largest K accepted: all codes +-127 give |sum| =
+    # 133120 * 127^2 = 2,147,092,480, just below 2^31, exact in int32
+    K = w8a8.POSTSCALE_MAX_K
+    assert K * 127 * 127 < 2 ** 31 <= (K + 128) * 127 * 127
+    x = np.full((128, K), 127.0, np.float32)
+    w = np.full((128, K), 127.0, np.float32)
+    w[1::2] = -127.0
+    qx, sx = oracle.quantize_rows(f32_to_bf16_bits(x))
+    qw, sw = oracle.quantize_rows(f32_to_bf16_bits(w))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    y = bf16_bits(w8a8.gemm_postscale(dev(qx), dev(sx), dev(qw), dev(sw)))
+    assert np.array_equal(y, oracle.linear_postscale(qx, sx, qw, sw))
+    # one K-block more is refused (the guarded linear falls back instead)
+    big = torch.zeros((128, K + 128), dtype=torch.int8, device="cuda")
+    sc = torch.ones(128, dtype=torch.float32, device="cuda")
+    with pytest.raises(w8a8.W8A8Error):
+        w8a8.gemm_postscale(big, sc, big, sc)
