@@ -53,7 +53,11 @@
 // The weight fragment is the MFMA "A" operand and the activation fragment
 // the "B" operand, so each lane holds 4 consecutive output columns n of one
 // row m per register group.  The output goes through LDS (free after the
-// main loop) so that Y is written in whole 256-byte row segments.
+// main loop) so that Y is written in whole 256-byte row segments, with
+// nontemporal stores: this kernel never reads Y back, and lines of it left
+// dirty in the last-level cache would be written back to HBM during the next
+// kernel (in a layer sequence, the next activation quantization), which then
+// ran 25% slower.
 //
 // The partials mode is the test epilogue: the same main loop stores P itself.
 //
@@ -371,7 +375,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
         for (int it = 0; it < kWaveM / 4; ++it) {
             const int row = it * 4 + (lane >> 4);
             const i32x4 v = *reinterpret_cast<const i32x4 *>(ot + row * 256 + ((c ^ (row & 15)) << 4));
-            if (row < rows_left) *reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N) = v;
+            if (row < rows_left)
+                __builtin_nontemporal_store(v, reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N));
         }
     }
 }

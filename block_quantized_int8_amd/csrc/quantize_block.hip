@@ -10,7 +10,9 @@
 // Memory-bound: one HBM read of the bf16 block (32 KiB) and one write of the
 // int8 block (16 KiB) plus one fp32 scale.  Each of the 256 threads holds 64
 // values (8 x 16-byte loads, all issued before any use) so the block is
-// never re-read; the absmax is taken on the magnitude bits (for non-negative
+// never re-read (nontemporal loads: x is not needed again, and keeping it
+// out of the last-level cache leaves room there for the codes, which the
+// GEMM reads next); the absmax is taken on the magnitude bits (for non-negative
 // floats the bit order is the value order), reduced across the wavefront
 // with lane shuffles and across the 4 wavefronts through LDS.
 //
@@ -51,7 +53,8 @@ __global__ __launch_bounds__(kThreads) void quantize_block_kernel(const uint16_t
     u32x4 v[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
-        v[p] = *reinterpret_cast<const u32x4 *>(src + (int64_t)p * kRowsPerPass * cols);
+        v[p] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(src + (int64_t)p * kRowsPerPass * cols));
 
     // absmax on the 15 magnitude bits of each bf16, two lanes of 16 bits at once
     uint32_t mhi = 0, mlo = 0;
