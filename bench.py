@@ -120,6 +120,32 @@ def cpu_model():
     return "unknown"
 
 
+def vendor_int8_context(qx, qw):
+    """The ROCm BLAS library's plain INT8 GEMM (torch._int_mm: int32 out, no
+    scales, no bf16 conversion) on the same operands: context for the
+    roofline fraction, not part of the path.  None if torch lacks it."""
+    import torch
+    try:
+        torch._int_mm(qx, qw.t())  # untimed first launch
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            torch._int_mm(qx, qw.t())
+        e1.record()
+        torch.cuda.synchronize()
+    except (RuntimeError, AttributeError) as exc:
+        log(f"vendor int8 GEMM unavailable: {exc}")
+        return None
+    us = e0.elapsed_time(e1) / reps * 1e3
+    tops = GEMM_OPS / (us * 1e-6) / 1e12
+    log(f"vendor plain int8 GEMM (torch._int_mm): {us:.1f} us = {tops:.0f} TOPS")
+    return {"note": "torch._int_mm on the same int8 operands (ROCm BLAS library; int32 output, no scales): "
+                    "context only", "us": round(us, 2), "tops": round(tops, 1),
+            "frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
+
+
 def cpu_baseline(d):
     """The oracle (untuned) on the first CPU_SAMPLE_BLOCKS row-blocks of X:
     quantize those rows and compute their full output rows."""
@@ -461,6 +487,7 @@ def main():
     torch.cuda.synchronize()
     ps_quant_ms = sum(a.elapsed_time(b) for a, b in pq) / args.steps
     del qxp, qwp, flush
+    vendor = vendor_int8_context(qx, qw)
 
     gemm_tops = GEMM_OPS / (gemm_ms * 1e-3) / 1e12
     quant_gbs = QUANT_BYTES / (quant_ms * 1e-3) / 1e9
@@ -515,6 +542,7 @@ def main():
                          "gemm_tops": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12, 1),
                          "gemm_frac_of_int8_peak": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                          "quantize_rows_us": round(ps_quant_ms * 1e3, 2)},
+        "vendor_int8_context": vendor,
         "two_stream": {"note": "A: INT8 linear 65536x4096x4096 (0.5% channels x30); B: 1000x2048x2048 "
                                "guarded to the bf16 fallback; launched on two streams per step (not the headline)",
                        "step_us": round(ts_both, 2), "a_alone_us": round(ts_a, 2), "b_alone_us": round(ts_b, 2)},

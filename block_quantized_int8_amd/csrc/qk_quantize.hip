@@ -16,7 +16,9 @@
 // One 256-thread workgroup per block, launched token block by token block
 // (all heads of a block, then the next block): each token row of D bf16 values is
 // D/8 16-byte chunks, so a pass covers 256/(D/8) rows and the 128 rows take
-// 128*D/2048 passes, every load issued before the first use.  Rows past L
+// 128*D/2048 passes, every load issued before the first use (nontemporal:
+// the projection output is not re-read, so it need not displace anything
+// in the last-level cache).  Rows past L
 // are neither read nor written.  Memory-bound, like the 128x128 quantizer.
 #include "quant_math.h"
 #include "w8a8_internal.h"
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(const uint16_t *_
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
         v[p] = l0 + p * kRowsPerPass < L
-                   ? *reinterpret_cast<const u32x4 *>(src + (int64_t)p * kRowsPerPass * ld)
+                   ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (int64_t)p * kRowsPerPass * ld))
                    : u32x4{0u, 0u, 0u, 0u};
 
     uint32_t m = 0;

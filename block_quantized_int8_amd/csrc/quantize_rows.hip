@@ -7,8 +7,8 @@
 // One wavefront per row, four rows per workgroup; no LDS and no barrier.
 // Rows of up to 16384 elements stay in registers: each lane holds kChunks
 // chunks of 8 bf16 (the smallest power of two that covers the row, all
-// loaded back to back), so X is read once; longer rows take a second pass
-// over the row for the codes.  The absmax is taken on the magnitude bits and
+// loaded back to back, nontemporal: X is not needed again), so X is read
+// once; longer rows take a second pass over the row for the codes.  The absmax is taken on the magnitude bits and
 // reduced with lane shuffles.  Division and rounding: quant_math.h; the
 // floor keeps s >= 2^-21, far above the range that needs a prescale, and
 // the scheme was checked against correctly rounded division for every bf16
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void quantize_rows_kernel(cons
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int64_t ch = (int64_t)c * 64 + lane;
-            v[c] = (kFull || ch < chunks) ? src[ch] : u32x4{0u, 0u, 0u, 0u};
+            v[c] = (kFull || ch < chunks) ? __builtin_nontemporal_load(&src[ch]) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) m = max(m, chunk_absmax_bits(v[c]));
