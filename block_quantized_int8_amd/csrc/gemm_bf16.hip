@@ -16,11 +16,13 @@
 // loaded one by one (per operand: the weight's loads are vectorized
 // whenever K % 8 == 0 and it is 16-byte aligned).
 //
-// This general kernel serves the calls the faster one cannot: bf16 input
+// This general kernel serves the calls the faster two cannot.  bf16 input
 // with K a multiple of 64, N a multiple of 128, 16-byte aligned operands and
 // at least 256 output tiles of 256x256 (any M, e.g. a token count that is
 // not a multiple of 128) goes to the 256x256-tile kernel of the INT8 path in
-// its bf16 mode (launch_gemm_bf16_tiled).
+// its bf16 mode (launch_gemm_bf16_tiled); other bf16 problems with K a
+// multiple of 64, N a multiple of 8 and aligned operands go to the
+// pipelined 64x128-tile kernel below (gemm_bf16_pipe_kernel).
 #include "w8a8_internal.h"
 
 namespace w8a8 {
@@ -178,6 +180,153 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const void *__restr
         }
 }
 
+// ---- pipelined kernel for bf16 problems too small for 256x256 tiles
+//
+// 64 (m) x 128 (n) output tile per workgroup of 4 wavefronts (32 x 64 each,
+// two independent accumulator chains per wavefront), 64-deep K steps.  With
+// few tiles per CU every K step is short, so load latency, not the matrix
+// cores, sets the pace; operands therefore go global -> LDS directly
+// (buffer_load_dwordx4 ... lds, range-checked: rows past M or N read as
+// zeros) into a ring of kStages stages, kStages - 1 steps ahead of the MFMAs;
+// the range check covers the scalar offset as well (checked on gfx950), so
+// the row-group offset may sit there.
+// LDS rows are 128 bytes with the INT8 kernel's chunk swizzle, so each MFMA
+// fragment is one conflict-free 16-byte read.
+constexpr int kPM = 64, kPN = 128;
+constexpr int kPThreads = 256;
+constexpr int kPRowBytes = 128;                            // 64 bf16 of K per LDS row
+constexpr int kPStageBytes = (kPM + kPN) * kPRowBytes;     // 24 KiB
+constexpr int kPXLoads = kPM / 8 / 4, kPWLoads = kPN / 8 / 4;  // 8-row DMA instructions per wave per step
+constexpr int kPLoads = kPXLoads + kPWLoads;
+constexpr int kPipeStages = 3;  // 72 KiB: two workgroups per CU (6 stages, one per CU, was slower)
+
+__device__ __forceinline__ int pswz(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
+
+// s_waitcnt with only a vector-memory count (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt at their no-wait maxima)
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | (7 << 4) | (15 << 8) | ((kVm >> 4) << 14));
+}
+
+template <int kStages>
+__global__ __launch_bounds__(kPThreads) void gemm_bf16_pipe_kernel(const uint16_t *__restrict__ x,
+                                                                   const uint16_t *__restrict__ w,
+                                                                   const uint16_t *__restrict__ bias,
+                                                                   uint16_t *__restrict__ y, int64_t M, int64_t N,
+                                                                   int64_t K, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kPStageBytes];
+    typedef __attribute__((address_space(3))) void *lds_ptr_t;
+    const int t = blockIdx.x;
+    const int mb = t / tiles_n, nb = t - mb * tiles_n;
+    const int64_t m0 = (int64_t)mb * kPM, n0 = (int64_t)nb * kPN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t row_bytes = K * 2;
+    const int KS = (int)(K / 64);
+
+    // operand tiles as buffers: loads past the last row of X or W return zeros
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x + m0 * K), (short)0, (int)(min((int64_t)kPM, M - m0) * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(w + n0 * K), (short)0, (int)(min((int64_t)kPN, N - n0) * row_bytes), 0x00020000);
+    // one DMA instruction fills 8 rows (1 KiB, lane-linear in LDS); lane l
+    // writes slot l%8 of row l/8, which holds global chunk pswz(row, l%8);
+    // the slot pattern depends on bit 3 of the row, i.e. on the parity of
+    // the 8-row group
+    uint32_t voff[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+        voff[b] = (uint32_t)((lane >> 3) * row_bytes) + (uint32_t)(pswz((lane >> 3) + 8 * b, lane & 7) * 16);
+    auto issue = [&](int step) {
+        uint8_t *st = lds + (step % kStages) * kPStageBytes;
+#pragma unroll
+        for (int i = 0; i < kPXLoads; ++i) {
+            const int g = wave * kPXLoads + i;  // 8-row group of X
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(st + g * 1024), 16, voff[g & 1],
+                                                     (int)(g * 8 * row_bytes + step * kPRowBytes), 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kPWLoads; ++i) {
+            const int g = wave * kPWLoads + i;  // 8-row group of W
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + kPM * kPRowBytes + g * 1024), 16,
+                                                     voff[g & 1], (int)(g * 8 * row_bytes + step * kPRowBytes),
+                                                     0, 0);
+        }
+    };
+
+    const int frow = lane & 31, fhalf = lane >> 5;
+    int fofs[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) fofs[kk] = frow * kPRowBytes + (pswz(frow, kk * 2 + fhalf) << 4);
+    const int xo = wm * 32 * kPRowBytes, wo = kPM * kPRowBytes + wn * 64 * kPRowBytes;
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < KS) issue(s);
+    for (int k = 0; k < KS; ++k) {
+        // this wave's loads of step k are done once at most the later
+        // in-flight steps' loads remain; the barrier then covers every
+        // wave's loads and every wave's reads of the stage refilled next
+        if (k + kStages - 2 < KS)
+            wait_vmcnt<kPLoads * (kStages - 2)>();
+        else
+            wait_vmcnt<0>();
+        // a bare s_barrier: __syncthreads' release fence would also wait
+        // for the younger steps' loads and undo the pipelining (every
+        // fragment read of a step is consumed by its MFMAs within the step,
+        // so no LDS read is outstanding here)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (k + kStages - 1 < KS) issue(k + kStages - 1);
+        const uint8_t *st = lds + (k % kStages) * kPStageBytes;
+        bf16x8 fx[4], fw[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            fx[kk] = *reinterpret_cast<const bf16x8 *>(st + xo + fofs[kk]);
+            fw[0][kk] = *reinterpret_cast<const bf16x8 *>(st + wo + fofs[kk]);
+            fw[1][kk] = *reinterpret_cast<const bf16x8 *>(st + wo + 32 * kPRowBytes + fofs[kk]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all 12 reads in flight before the first MFMA waits
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i][kk], fx[kk], acc[i], 0, 0, 0);
+    }
+
+    // lane: output row m = m0 + 32 wm + frow; register group q of sub-tile i
+    // holds columns n .. n+3, n = n0 + 64 wn + 32 i + 8 q + 4 fhalf
+    const int64_t m = m0 + wm * 32 + frow;
+    if (m >= M) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 64 + i * 32 + q * 8 + fhalf * 4;
+            if (n >= N) continue;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = acc[i][q * 4 + e];
+                if (bias) v[e] += __uint_as_float((uint32_t)bias[n + e] << 16);
+            }
+            u32x2 out;
+            out.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+            out.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<u32x2 *>(y + m * N + n) = out;
+        }
+}
+
 template <int kDtype, bool kVecX, bool kVecW>
 hipError_t launch_typed(const void *x, const uint16_t *w, const uint16_t *bias, int64_t M, int64_t N,
                         int64_t K, uint16_t *y, hipStream_t stream) {
@@ -200,6 +349,15 @@ hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const
     if (x_dtype == 0 && K % 64 == 0 && K <= (1 << 21) && N % 128 == 0 && a16 && (uintptr_t)bias % 8 == 0 &&
         big_tiles >= 256)
         return launch_gemm_bf16_tiled(static_cast<const uint16_t *>(x), w, bias, M, N, K, y, stream);
+    // other bf16 problems with K a multiple of 64 and N of 8: the pipelined
+    // 64x128-tile kernel
+    if (x_dtype == 0 && K % 64 == 0 && K <= (1 << 21) && N % 8 == 0 && a16) {
+        const int64_t tm = (M + kPM - 1) / kPM, tn = (N + kPN - 1) / kPN;
+        if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+        gemm_bf16_pipe_kernel<kPipeStages><<<dim3((unsigned)(tm * tn)), dim3(kPThreads), 0, stream>>>(
+            static_cast<const uint16_t *>(x), w, bias, y, M, N, K, (int)tn);
+        return hipGetLastError();
+    }
     const bool vec_w = (K % 8 == 0) && ((uintptr_t)w % 16 == 0);
     const bool vec_x = (x_dtype == 0) && vec_w && ((uintptr_t)x % 16 == 0);
     if (vec_x) return launch_typed<0, true, true>(x, w, bias, M, N, K, y, stream);

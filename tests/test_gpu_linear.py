@@ -137,3 +137,22 @@ def test_fallback_large_tiled(M, K, N):
                                      np.random.default_rng(M).integers(0, M, 200)]))
     assert_bf16_close(bf16_bits(y)[rows], oracle.linear_bf16(x, oracle.DTYPE_BF16, w, bias=b, rows=rows),
                       f"fallback {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(1000, 2048, 2048), (999, 64, 200), (65, 128, 8), (129, 320, 1000),
+                                   (3000, 1024, 1032), (64, 384, 128)])
+def test_fallback_pipelined(M, K, N):
+    # bf16 input, K a multiple of 64, N of 8, too few 256x256 tiles for the
+    # tiled kernel: the pipelined 64x128-tile kernel, from fewer K steps than
+    # its ring has stages (K = 64) to many more (K = 2048), ragged M and N
+    x = random_bf16(M + 2 * K, (M, K))
+    w = random_bf16(N + 2 * K, (N, K), 0.02)
+    b = random_bf16(N + 2, (N,), 0.1)
+    for bias in (None, b):
+        y, path = w8a8.linear(to_dev_bf16(x), to_dev_bf16(w), bias=None if bias is None else to_dev_bf16(bias))
+        torch.cuda.synchronize()
+        assert path == w8a8.PATH_BF16
+        rows = np.unique(np.concatenate([np.arange(0, min(M, 40)), np.arange(max(0, M - 40), M),
+                                         np.random.default_rng(M).integers(0, M, 60)]))
+        assert_bf16_close(bf16_bits(y)[rows], oracle.linear_bf16(x, oracle.DTYPE_BF16, w, bias=bias, rows=rows),
+                          f"pipelined fallback {M}x{K}x{N} bias={bias is not None}")
