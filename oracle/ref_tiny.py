@@ -1,0 +1,185 @@
+"""A second, independent oracle for tiny inputs, in numpy and plain Python.
+
+TEST INFRASTRUCTURE ONLY, like the C oracle beside it: the CPU tests run
+both on the same small seeded inputs and require identical codes, scales,
+partials and bf16 outputs, so that a slip in either one (an index, an
+operand order, a rounding step) shows up as a disagreement.  It shares no
+code with the C oracle or with the GPU library; it is written straight from
+the definitions:
+
+* block quantization (TurboDiffusion news article, bjdmk.com.cn, section on
+  sparsity, distillation and full-pipeline quantization and the inference
+  list: 128x128 blocks for weights and, at the same granularity, for
+  activations; TurboT2VA paper, architecture-aware inference stack, W8A8
+  paragraph: scale = max-abs / 127, INT8 codes);
+* the block-scaled product: exact integer sums inside each 128-deep K-block,
+  each scaled by its two block scales, summed in fp64 and rounded once to
+  bf16 (nearest, ties to even);
+* the bf16 fallback and the guard (TurboT2VA paper, guard paragraph);
+* the post-scale form (TurboT2VA paper, W8A8 paragraph: per-row and
+  per-output-channel max(max-abs, 1e-4) / 127, integer sum over all of K,
+  scales and bias once at the end);
+* INT8 attention Q/K (TurboT2VA paper, sparse-attention paragraph): the
+  block rule over 128 tokens x the head dimension, per batch and head.
+
+Everything is O(M*N*K) Python-level numpy on small arrays: use it on
+inputs of a few hundred rows at most.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 128
+EPS = np.float32(1e-4)
+
+
+# ---------------------------------------------------------------- bf16 bits
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 values (a bf16 is the top half of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _round_half_even(v: float) -> float:
+    f = math.floor(v)
+    d = v - f  # exact: v and f are within one unit of each other
+    if d > 0.5 or (d == 0.5 and f % 2 == 1):
+        f += 1
+    return float(f)
+
+
+def f64_to_bf16_bits(v: float) -> int:
+    """Round one finite float64 to bf16 (nearest, ties to even), directly
+    rather than through fp32 (which could round twice)."""
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    _, e = math.frexp(a)           # a = m * 2^e with 0.5 <= m < 1
+    # bf16 keeps 8 significant bits; below 2^-126 the spacing stays 2^-133
+    ulp_exp = max(e - 8, -133)
+    r = _round_half_even(math.ldexp(a, -ulp_exp))   # exact scaling by a power of two
+    val = math.ldexp(r, ulp_exp)
+    bits = int(np.array([val], dtype=np.float32).view(np.uint32)[0] >> 16)
+    return sign | bits
+
+
+def f64_to_bf16_array(a: np.ndarray) -> np.ndarray:
+    flat = [f64_to_bf16_bits(float(v)) for v in np.asarray(a, dtype=np.float64).ravel()]
+    return np.array(flat, dtype=np.uint16).reshape(np.shape(a))
+
+
+# ------------------------------------------------------------- quantization
+
+def _codes(x32: np.ndarray, s: np.float32) -> np.ndarray:
+    """q = rint(fl32(x / s)), ties to even, clamped to [-127, 127]; s = 0 -> 0."""
+    if s == 0:
+        return np.zeros(x32.shape, np.int8)
+    quo = (x32 / s).astype(np.float32)          # IEEE fp32 division, one rounding
+    return np.clip(np.rint(quo), -127, 127).astype(np.int8)
+
+
+def quantize_block(x_bits: np.ndarray):
+    """128x128 block quantization of a bf16 matrix -> (q int8, s fp32 [R/128, C/128])."""
+    x32 = bf16_to_f64(x_bits).astype(np.float32)    # exact
+    R, C = x32.shape
+    q = np.zeros((R, C), np.int8)
+    s = np.zeros((R // BLOCK, C // BLOCK), np.float32)
+    for i in range(R // BLOCK):
+        for j in range(C // BLOCK):
+            blk = x32[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK]
+            a = np.float32(np.max(np.abs(blk)))
+            sc = np.float32(a / np.float32(127.0))
+            s[i, j] = sc
+            q[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK] = _codes(blk, sc)
+    return q, s
+
+
+def kblock_partials(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """P[m, n, kb] = sum over the K-block of qx[m, k] * qw[n, k], exact (int64)."""
+    M, K = qx.shape
+    kbs = K // BLOCK
+    a = qx.astype(np.int64).reshape(M, kbs, BLOCK)
+    b = qw.astype(np.int64).reshape(qw.shape[0], kbs, BLOCK)
+    return np.einsum("mkb,nkb->mnk", a, b)
+
+
+def linear_int8(qx, sx, qw, sw, bias=None) -> np.ndarray:
+    """bf16( sum_kb P * sx[m/128, kb] * sw[n/128, kb] (+ bias) ), fp64 sums in K-block order."""
+    P = kblock_partials(qx, qw).astype(np.float64)
+    M, N, kbs = P.shape
+    sxd = np.asarray(sx, np.float32).astype(np.float64)
+    swd = np.asarray(sw, np.float32).astype(np.float64)
+    rowblk = np.arange(M) // BLOCK
+    colblk = np.arange(N) // BLOCK
+    acc = np.zeros((M, N), np.float64)
+    for kb in range(kbs):
+        acc = acc + P[:, :, kb] * sxd[rowblk, kb][:, None] * swd[colblk, kb][None, :]
+    if bias is not None:
+        acc = acc + bf16_to_f64(bias)[None, :]
+    return f64_to_bf16_array(acc)
+
+
+def linear_bf16(x_bits, w_bits, bias=None) -> np.ndarray:
+    """The fallback on bf16 input: bf16( sum_k x * w (+ bias) ) with fp64 sums."""
+    acc = bf16_to_f64(x_bits) @ bf16_to_f64(w_bits).T
+    if bias is not None:
+        acc = acc + bf16_to_f64(bias)[None, :]
+    return f64_to_bf16_array(acc)
+
+
+def route(is_bf16: bool, M: int, K: int, N: int, has_qweight: bool) -> int:
+    """0 (INT8 path) iff bf16 input, M, K, N multiples of 128 and a quantized weight; else 1."""
+    ok = is_bf16 and has_qweight and M > 0 and K > 0 and N > 0 and M % BLOCK == 0 \
+        and K % BLOCK == 0 and N % BLOCK == 0
+    return 0 if ok else 1
+
+
+# ------------------------------------------------------------ post-scale form
+
+def quantize_rows(x_bits: np.ndarray):
+    """Per-row s = fl32(max(max-abs, 1e-4) / 127), q = rint(fl32(x / s))."""
+    x32 = bf16_to_f64(x_bits).astype(np.float32)
+    q = np.zeros(x32.shape, np.int8)
+    s = np.zeros(x32.shape[0], np.float32)
+    for i in range(x32.shape[0]):
+        a = np.float32(max(np.float32(np.max(np.abs(x32[i]))), np.float32(EPS)))
+        s[i] = np.float32(a / np.float32(127.0))
+        q[i] = _codes(x32[i], s[i])
+    return q, s
+
+
+def linear_postscale(qx, sx, qw, sw, bias=None) -> np.ndarray:
+    """bf16( (sum_k qx * qw) * sx[m] * sw[n] (+ bias) ): integer sum over all of K."""
+    acc = (qx.astype(np.int64) @ qw.astype(np.int64).T).astype(np.float64)
+    acc = acc * np.asarray(sx, np.float32).astype(np.float64)[:, None] \
+        * np.asarray(sw, np.float32).astype(np.float64)[None, :]
+    if bias is not None:
+        acc = acc + bf16_to_f64(bias)[None, :]
+    return f64_to_bf16_array(acc)
+
+
+# ---------------------------------------------------------- attention Q / K
+
+def quantize_qk(x_bits: np.ndarray, B: int, L: int, H: int, D: int, ld: int):
+    """Rows b*L + l of width ld hold token l of batch b, head h at columns
+    h*D .. h*D + D-1.  Each (b, h) is cut into blocks of 128 tokens (the last
+    may be shorter), each quantized by the block rule over tokens x D.
+    -> (q int8 [B, H, L, D], s fp32 [B, H, ceil(L/128)])."""
+    x = np.asarray(x_bits, np.uint16).reshape(B * L, ld)
+    nblk = -(-L // BLOCK)
+    q = np.zeros((B, H, L, D), np.int8)
+    s = np.zeros((B, H, nblk), np.float32)
+    for b in range(B):
+        for h in range(H):
+            head = bf16_to_f64(x[b * L:(b + 1) * L, h * D:(h + 1) * D]).astype(np.float32)
+            for j in range(nblk):
+                blk = head[j * BLOCK:min((j + 1) * BLOCK, L)]
+                a = np.float32(np.max(np.abs(blk)))
+                sc = np.float32(a / np.float32(127.0))
+                s[b, h, j] = sc
+                q[b, h, j * BLOCK:j * BLOCK + blk.shape[0]] = _codes(blk, sc)
+    return q, s
