@@ -1,0 +1,101 @@
+// Exercises the host side of libw8a8 (include/w8a8.h) with AddressSanitizer
+// and UndefinedBehaviorSanitizer on the host code (tests/test_sanitizers.py):
+// the guard over a grid, the workspace sizes, the status strings and every
+// argument error that is decided before any device work.  It links the
+// library's API source with stand-in launchers that abort if reached, so it
+// also proves that none of these calls gets as far as a kernel launch.
+#include <cstdio>
+#include <cstdlib>
+
+#include "w8a8.h"
+#include "w8a8_internal.h"
+
+[[noreturn]] static void reached(const char *what) {
+    std::fprintf(stderr, "unexpected launch: %s\n", what);
+    std::abort();
+}
+
+namespace w8a8 {
+hipError_t launch_quantize_block(const uint16_t *, int64_t, int64_t, int8_t *, float *, hipStream_t) { reached("quantize_block"); }
+hipError_t launch_gemm_i8_blockscale(const int8_t *, const float *, const int8_t *, const float *, const uint16_t *,
+                                     int64_t, int64_t, int64_t, uint16_t *, hipStream_t) { reached("gemm_i8_blockscale"); }
+hipError_t launch_kblock_partials(const int8_t *, const int8_t *, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
+                                  int64_t, int32_t *, hipStream_t) { reached("kblock_partials"); }
+hipError_t launch_quantize_rows(const uint16_t *, int64_t, int64_t, int8_t *, float *, hipStream_t) { reached("quantize_rows"); }
+hipError_t launch_gemm_i8_postscale(const int8_t *, const float *, const int8_t *, const float *, const uint16_t *,
+                                    int64_t, int64_t, int64_t, uint16_t *, hipStream_t) { reached("gemm_i8_postscale"); }
+hipError_t launch_gelu_bf16(const uint16_t *, int64_t, uint16_t *, hipStream_t) { reached("gelu_bf16"); }
+hipError_t launch_gelu_quantize_block(const uint16_t *, int64_t, int64_t, int8_t *, float *, hipStream_t) { reached("gelu_quantize"); }
+hipError_t launch_quantize_qk(const uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t, int8_t *, float *,
+                              hipStream_t) { reached("quantize_qk"); }
+hipError_t launch_gemm_bf16_tiled(const uint16_t *, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t,
+                                  uint16_t *, hipStream_t) { reached("gemm_bf16_tiled"); }
+hipError_t launch_gemm_bf16(const void *, int, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t, uint16_t *,
+                            hipStream_t) { reached("gemm_bf16"); }
+}  // namespace w8a8
+
+#define CHECK(cond)                                                                    \
+    do {                                                                               \
+        if (!(cond)) {                                                                 \
+            std::fprintf(stderr, "check failed: %s (line %d)\n", #cond, __LINE__);     \
+            return 1;                                                                  \
+        }                                                                              \
+    } while (0)
+
+int main() {
+    // the guard: INT8 iff bf16, M, K, N multiples of 128 and a quantized weight
+    const long long dims[] = {-128, 0, 1, 127, 128, 130, 256, 4000, 4096};
+    for (int dt = -1; dt <= 3; ++dt)
+        for (long long m : dims)
+            for (long long k : dims)
+                for (long long n : dims)
+                    for (int hq = 0; hq <= 1; ++hq) {
+                        const int r = w8a8_route(dt, m, k, n, hq);
+                        const bool bad = m <= 0 || k <= 0 || n <= 0 || dt < 0 || dt > 2;
+                        const bool int8 = !bad && dt == W8A8_DTYPE_BF16 && m % 128 == 0 && k % 128 == 0 &&
+                                          n % 128 == 0 && hq;
+                        CHECK(r == (bad ? -1 : int8 ? W8A8_PATH_INT8 : W8A8_PATH_BF16));
+                    }
+    // workspace sizes: 0 when the INT8 path cannot be taken, else 256-byte rounded pieces
+    CHECK(w8a8_linear_workspace_bytes(0, 128) == 0 && w8a8_linear_workspace_bytes(128, 100) == 0);
+    CHECK(w8a8_linear_workspace_bytes(128, 128) == 16384 + 256);
+    CHECK(w8a8_linear_postscale_workspace_bytes(256, 128) == 32768 + 1024);
+    CHECK(w8a8_linear_workspace_bytes((1LL << 40), 1LL << 20) > 0);
+    for (int st = -1; st <= 5; ++st) CHECK(w8a8_status_string(st) != nullptr);
+
+    // argument errors decided on the host (fake, never dereferenced, aligned addresses)
+    void *p = reinterpret_cast<void *>(0x10000);
+    int8_t *q8 = static_cast<int8_t *>(p);
+    float *f = static_cast<float *>(p);
+    int path = -7;
+    CHECK(w8a8_quantize_act(nullptr, 128, 128, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_quantize_act(p, 100, 128, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_quantize_weight(p, 128, -128, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_quantize_weight(static_cast<char *>(p) + 2, 128, 128, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gemm_blockscale(q8, f, q8, f, nullptr, 128, 130, 128, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gemm_blockscale(q8, nullptr, q8, f, nullptr, 128, 128, 128, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear(p, 7, 128, 128, 128, p, q8, f, nullptr, p, p, 1 << 20, nullptr, &path) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear(p, 0, 128, 128, 128, p, q8, nullptr, nullptr, p, p, 1 << 20, nullptr, &path) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear(p, 0, 0, 128, 128, p, nullptr, nullptr, nullptr, p, nullptr, 0, nullptr, &path) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(path == -7);  // untouched on an argument error
+    CHECK(w8a8_linear_postscale(nullptr, 0, 128, 128, 128, p, q8, f, nullptr, p, p, 0, nullptr, nullptr) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_debug_kblock_partials(q8, q8, 256, 256, 256, 128, 256, 0, 128, static_cast<int32_t *>(p), nullptr) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_debug_kblock_partials(q8, q8, 256, 256, 256, 64, 128, 0, 128, static_cast<int32_t *>(p), nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_quantize_rows(p, 128, 12, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gemm_postscale(q8, f, q8, f, nullptr, 128, 128, W8A8_POSTSCALE_MAX_K + 128, p, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gelu_bf16(p, 0, p, nullptr) == W8A8_OK);
+    CHECK(w8a8_gelu_bf16(p, -1, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_gelu_bf16(static_cast<char *>(p) + 1, 8, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gelu_quantize_act(p, 128, W8A8_GELU_QUANT_MAX_K + 128, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_quantize_qk(p, 1, 256, 2, 96, 192, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_quantize_qk(p, 1, 256, 2, 128, 255, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_quantize_qk(p, 1LL << 40, 256, 1LL << 20, 128, 1LL << 27, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    std::printf("host sanitizer driver: ok\n");
+    return 0;
+}
