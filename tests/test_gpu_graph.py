@@ -1,0 +1,95 @@
+"""The library under HIP graph capture.
+
+Every entry point only enqueues kernels on the caller's stream and never
+allocates, copies or synchronizes, so a whole layer step can be captured
+once and replayed.  Each test captures the calls with preallocated buffers,
+then replays the graph several times with new inputs written eagerly in
+between, and checks every replay bit for bit against an eager call on the
+same input (and one replay against the oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_int8_amd as w8a8
+import oracle
+from block_quantized_int8_amd.workloads import random_bf16
+from parity import assert_bf16_close, bf16_bits, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                                   # eager warm-up off the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("M,K,N,int8", [(512, 256, 384, True), (1000, 256, 384, False)])
+def test_linear_step_replays(M, K, N, int8):
+    w = to_dev_bf16(random_bf16(31, (N, K), 0.02))
+    b = to_dev_bf16(random_bf16(32, (N,), 0.1))
+    layer = w8a8.W8A8Linear(w)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.copy_(to_dev_bf16(random_bf16(33, (M, K))))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(w8a8.workspace_bytes(M, K), 1), dtype=torch.uint8, device="cuda")
+    paths = []
+
+    def step():
+        _, path = w8a8.linear(x, w, layer.qweight, layer.wscale, bias=b, out=y, workspace=ws)
+        paths.append(path)
+
+    g = capture(step)
+    assert paths[-1] == (w8a8.PATH_INT8 if int8 else w8a8.PATH_BF16)
+    for seed in (34, 35, 36):
+        xh = random_bf16(seed, (M, K))
+        x.copy_(to_dev_bf16(xh))               # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        ref, _ = w8a8.linear(x, w, layer.qweight, layer.wscale, bias=b)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay with input seed {seed}"
+    wh = bf16_bits(w)
+    if int8:
+        qx, sx = oracle.quantize_block(xh)
+        qw, sw = oracle.quantize_block(wh)
+        want = oracle.linear_int8(qx, sx, qw, sw, bias=bf16_bits(b))
+    else:
+        want = oracle.linear_bf16(xh, oracle.DTYPE_BF16, wh, bias=bf16_bits(b))
+    assert_bf16_close(bf16_bits(got), want, f"graph replay {M}x{K}x{N}")
+
+
+def test_producer_and_qk_replay():
+    # fused GELU + quantize and INT8 Q/K in one graph
+    M, K, H, D = 256, 512, 4, 128
+    yh = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s = torch.empty((M // 128, K // 128), dtype=torch.float32, device="cuda")
+    kq = torch.empty((H, M, D), dtype=torch.int8, device="cuda")
+    ks = torch.empty((H, M // 128), dtype=torch.float32, device="cuda")
+
+    def work():
+        w8a8.gelu_quantize_act(yh, q, s)
+        w8a8.quantize_qk(yh, H, kq, ks)
+
+    yh.copy_(to_dev_bf16(random_bf16(40, (M, K))))
+    g = capture(work)
+    for seed in (41, 42):
+        host = random_bf16(seed, (M, K))
+        yh.copy_(to_dev_bf16(host))
+        g.replay()
+        torch.cuda.synchronize()
+        oq, os_ = oracle.gelu_quantize_block(host)
+        assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+        kq_o, ks_o = oracle.quantize_qk(host, 1, M, H, D, K)
+        assert np.array_equal(kq.cpu().numpy(), kq_o[0]) and np.array_equal(ks.cpu().numpy(), ks_o[0])
