@@ -26,6 +26,7 @@ EXPORTS = (
     "w8a8_linear_postscale", "w8a8_gelu_bf16", "w8a8_gelu_quantize_act", "w8a8_quantize_qk",
 )
 POSTSCALE_MAX_K = 133120
+BLOCK_MAX_K = 4194304
 GELU_QUANT_MAX_K = 8388480
 
 _P = ctypes.c_void_p

@@ -71,7 +71,7 @@ int w8a8_gemm_blockscale(const int8_t *qx, const float *sx, const int8_t *qw, co
                          const void *bias_bf16, int64_t M, int64_t N, int64_t K, void *y_bf16,
                          hipStream_t stream) {
     if (!qx || !sx || !qw || !sw || !y_bf16 || M <= 0 || N <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
-    if (!mult128(M) || !mult128(N) || !mult128(K)) return W8A8_ERR_UNSUPPORTED;
+    if (!mult128(M) || !mult128(N) || !mult128(K) || K > W8A8_BLOCK_MAX_K) return W8A8_ERR_UNSUPPORTED;
     if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(y_bf16, 16) || !aligned(sx, 4) ||
         !aligned(sw, 4) || !aligned(bias_bf16, 8))
         return W8A8_ERR_UNSUPPORTED;
@@ -101,6 +101,7 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, con
         return W8A8_ERR_INVALID_ARG;
 
     int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
+    if (path == W8A8_PATH_INT8 && K > W8A8_BLOCK_MAX_K) path = W8A8_PATH_BF16;
     if (path == W8A8_PATH_INT8) {
         const size_t need = w8a8_linear_workspace_bytes(M, K);
         if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
@@ -132,8 +133,8 @@ int w8a8_debug_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, in
                                hipStream_t stream) {
     if (!qx || !qw || !partials || M <= 0 || N <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
     if (m0 < 0 || n0 < 0 || mt <= 0 || nt <= 0 || m0 + mt > M || n0 + nt > N) return W8A8_ERR_INVALID_ARG;
-    if (!mult128(M) || !mult128(N) || !mult128(K) || m0 % W8A8_BLOCK || n0 % W8A8_BLOCK ||
-        mt % W8A8_BLOCK || nt % W8A8_BLOCK)
+    if (!mult128(M) || !mult128(N) || !mult128(K) || K > W8A8_BLOCK_MAX_K || m0 % W8A8_BLOCK ||
+        n0 % W8A8_BLOCK || mt % W8A8_BLOCK || nt % W8A8_BLOCK)
         return W8A8_ERR_UNSUPPORTED;
     if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(partials, 4)) return W8A8_ERR_UNSUPPORTED;
     if (!is_device_ptr(qx) || !is_device_ptr(qw) || !is_device_ptr(partials)) return W8A8_ERR_INVALID_ARG;

@@ -60,6 +60,10 @@ enum { W8A8_DTYPE_BF16 = 0, W8A8_DTYPE_FP16 = 1, W8A8_DTYPE_FP32 = 2 };
 enum { W8A8_PATH_INT8 = 0, W8A8_PATH_BF16 = 1 };
 #define W8A8_BLOCK 128
 
+/* Largest K of the block-scale GEMM: it addresses a 256-row operand tile
+ * with 32-bit byte offsets (256 * K < 2^31). */
+#define W8A8_BLOCK_MAX_K 4194304
+
 /*
  * Static weight quantization (done once, at load): w_bf16 [N, K] ->
  * qw int8 [N, K] and sw fp32 [N/128, K/128].
@@ -85,8 +89,8 @@ int w8a8_quantize_act(const void *x_bf16, int64_t M, int64_t K, int8_t *qx, floa
  *                 qx[m, k] * qw[n, k].
  * The sum over K-blocks is carried in fp32; bias (bf16 [N], nullable) is
  * added in fp32; Y is bf16 [M, N], rounded to nearest even.
- * Strict: M, N, K multiples of 128 and qx, qw, y 16-byte aligned, else
- * W8A8_ERR_UNSUPPORTED.
+ * Strict: M, N, K multiples of 128, K <= W8A8_BLOCK_MAX_K and qx, qw, y
+ * 16-byte aligned, else W8A8_ERR_UNSUPPORTED.
  */
 int w8a8_gemm_blockscale(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
                          const void *bias_bf16, int64_t M, int64_t N, int64_t K, void *y_bf16,
@@ -110,8 +114,9 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
  *   workspace: >= w8a8_linear_workspace_bytes(M, K) bytes when the INT8
  *              path is taken (may be null/0 otherwise)
  *   path_out : if not null, receives the W8A8_PATH_* taken
- * INT8 path iff w8a8_route(...) == W8A8_PATH_INT8 and x, y, qw and the
- * workspace are 16-byte aligned: then the activation is quantized into the
+ * INT8 path iff w8a8_route(...) == W8A8_PATH_INT8, K <= W8A8_BLOCK_MAX_K
+ * and x, y, qw and the workspace are 16-byte aligned: then the activation
+ * is quantized into the
  * workspace and w8a8_gemm_blockscale's computation runs.  Otherwise the bf16
  * fallback runs: Y = bf16( sum_k bf16(x[m,k]) * w[n,k] (+ bias[n]) ) with
  * fp32 accumulation; fp16/fp32 x is rounded to bf16 (nearest even) on load.
@@ -137,7 +142,7 @@ int w8a8_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight);
  * exact int32 per-K-block partials instead of dequantizing them.
  * Window rows [m0, m0+mt) of qx and [n0, n0+nt) of qw; m0, mt, n0, nt
  * multiples of 128 inside the matrices; partials int32 [mt, nt, K/128].
- * Strict shape/alignment rules as w8a8_gemm_blockscale.
+ * Strict shape/alignment rules (and K limit) as w8a8_gemm_blockscale.
  */
 int w8a8_debug_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N, int64_t K,
                                int64_t m0, int64_t mt, int64_t n0, int64_t nt, int32_t *partials,

@@ -74,6 +74,10 @@ int main() {
     CHECK(w8a8_quantize_weight(static_cast<char *>(p) + 2, 128, 128, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_gemm_blockscale(q8, f, q8, f, nullptr, 128, 130, 128, p, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_gemm_blockscale(q8, nullptr, q8, f, nullptr, 128, 128, 128, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_gemm_blockscale(q8, f, q8, f, nullptr, 128, 128, W8A8_BLOCK_MAX_K + 128, p, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_debug_kblock_partials(q8, q8, 128, 128, W8A8_BLOCK_MAX_K + 128, 0, 128, 0, 128,
+                                     static_cast<int32_t *>(p), nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_linear(p, 7, 128, 128, 128, p, q8, f, nullptr, p, p, 1 << 20, nullptr, &path) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_linear(p, 0, 128, 128, 128, p, q8, nullptr, nullptr, p, p, 1 << 20, nullptr, &path) ==
           W8A8_ERR_INVALID_ARG);

@@ -156,3 +156,19 @@ def test_fallback_pipelined(M, K, N):
                                          np.random.default_rng(M).integers(0, M, 60)]))
         assert_bf16_close(bf16_bits(y)[rows], oracle.linear_bf16(x, oracle.DTYPE_BF16, w, bias=bias, rows=rows),
                           f"pipelined fallback {M}x{K}x{N} bias={bias is not None}")
+
+
+def test_block_gemm_k_limit_routes_to_fallback():
+    # K just past the block GEMM's limit: the guarded linear takes the bf16
+    # fallback (never a silently wrong INT8 result); one output row vs the oracle
+    from block_quantized_int8_amd._lib import BLOCK_MAX_K
+    M, N, K = 128, 128, BLOCK_MAX_K + 128
+    x = random_bf16(71, (M, K))
+    w = random_bf16(72, (N, K), 0.02)
+    wd = to_dev_bf16(w)
+    qw, sw = w8a8.quantize_weight(wd)
+    y, path = w8a8.linear(to_dev_bf16(x), wd, qw, sw)
+    torch.cuda.synchronize()
+    assert path == w8a8.PATH_BF16
+    rows = np.array([0, 77], np.int64)
+    assert_bf16_close(bf16_bits(y)[rows], oracle.linear_bf16(x, oracle.DTYPE_BF16, w, rows=rows), "K past the limit")

@@ -83,6 +83,10 @@ def test_host_decided_errors(L):
     assert L.w8a8_quantize_act(ctypes.c_void_p(0x1002), 128, 128, fake, fake, null) == 2
     assert L.w8a8_gemm_blockscale(fake, fake, fake, fake, null, 4000, 128, 128, fake, null) == 2
     assert L.w8a8_gemm_blockscale(null, fake, fake, fake, null, 128, 128, 128, fake, null) == 1
+    # K beyond the block GEMM's 32-bit tile addressing
+    from block_quantized_int8_amd._lib import BLOCK_MAX_K
+    assert L.w8a8_gemm_blockscale(fake, fake, fake, fake, null, 128, 128, BLOCK_MAX_K + 128, fake, null) == 2
+    assert L.w8a8_debug_kblock_partials(fake, fake, 128, 128, BLOCK_MAX_K + 128, 0, 128, 0, 128, fake, null) == 2
     # linear: missing weight copy, unknown dtype, half a quantized weight
     path = ctypes.c_int(-7)
     assert L.w8a8_linear(fake, 0, 128, 128, 128, null, null, null, null, fake, null, 0, null,
