@@ -207,7 +207,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
