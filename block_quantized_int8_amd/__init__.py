@@ -124,6 +124,63 @@ def gelu_quantize_act(y: torch.Tensor, q=None, s=None):
     return _quantize(lib().w8a8_gelu_quantize_act, "y", y, q, s)
 
 
+def _modulation_args(x, scale, shift):
+    """x bf16 [B, L, K] (or [L, K] with B = 1), scale and shift bf16 [B, K]."""
+    _need_cuda("x", x, torch.bfloat16)
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    if x3.dim() != 3:
+        raise ValueError("x must be [B, L, K] or [L, K]")
+    B, L, K = x3.shape
+    for name, t in (("scale", scale), ("shift", shift)):
+        _need_cuda(name, t, torch.bfloat16)
+        if t.numel() != B * K:
+            raise ValueError(f"{name} must hold B*K = {B * K} values ([B, K])")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not x3.is_contiguous():
+        x3 = x3.contiguous()
+    return x3, B, L, K
+
+
+def rmsnorm_modulate_bf16(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6,
+                          out=None):
+    """Modulated RMS normalization of bf16 x [B, L, K] with per-batch scale and
+    shift [B, K]: bf16(x * r * (1 + scale) + shift), r = 1/sqrt(mean(x^2) + eps)."""
+    x3, B, L, K = _modulation_args(x, scale, shift)
+    if out is None:
+        out = torch.empty_like(x)
+    _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != x3.numel() or not out.is_contiguous():
+        raise ValueError("out must be contiguous with as many elements as x")
+    r = torch.empty(B * L, dtype=torch.float32, device=x.device)   # the entry point's workspace
+    check("w8a8_rmsnorm_modulate_bf16",
+          lib().w8a8_rmsnorm_modulate_bf16(_ptr(x3), B, L, K, _ptr(scale), _ptr(shift), float(eps), _ptr(r),
+                                           _ptr(out), _stream(x.device)))
+    return out
+
+
+def rmsnorm_modulate_quantize_act(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6,
+                                  q=None, s=None):
+    """Block quantization of the modulated RMS normalization of x [B, L, K],
+    fused (the bf16 result is never written) -> (q int8 [B*L, K],
+    s fp32 [B*L/128, K/128])."""
+    x3, B, L, K = _modulation_args(x, scale, shift)
+    M = B * L
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = torch.empty((max(M // BLOCK, 1), max(K // BLOCK, 1)), dtype=torch.float32, device=x.device)
+    _need_cuda("q", q, torch.int8)
+    _need_cuda("s", s, torch.float32)
+    if q.numel() != M * K or s.numel() < (M // BLOCK) * (K // BLOCK):
+        raise ValueError("output buffers have the wrong size")
+    r = torch.empty(M, dtype=torch.float32, device=x.device)       # the entry point's workspace
+    check("w8a8_rmsnorm_modulate_quantize_act",
+          lib().w8a8_rmsnorm_modulate_quantize_act(_ptr(x3), B, L, K, _ptr(scale), _ptr(shift), float(eps),
+                                                   _ptr(r), _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
 def quantize_qk(x: torch.Tensor, heads: int, q=None, s=None):
     """INT8 attention Q or K: ``x`` is bf16 [B, L, H*D] or [L, H*D],
     sequence-major, with unit stride in the last dimension (a column slice
@@ -345,6 +402,34 @@ class W8A8Linear(torch.nn.Module):
         out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
         self.last_path = PATH_INT8
         return out.view(*y.shape[:-1], N)
+
+
+    def forward_modulated(self, x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                          eps: float = 1e-6) -> torch.Tensor:
+        """``self(rmsnorm_modulate_bf16(x, scale, shift, eps))`` for bf16 x
+        [B, L, K]: the modulated normalization fused into the input
+        quantization when the INT8 block path applies; otherwise it runs
+        alone and ``forward`` takes its own guarded path."""
+        N, K = self.weight.shape
+        x3, B, L, Kx = _modulation_args(x, scale, shift)
+        if Kx != K:
+            raise ValueError(f"last dimension of x must be {K}")
+        M = B * L
+        fused = (self.scaling == "block" and self.qweight is not None
+                 and route(torch.bfloat16, M, K, N, True) == PATH_INT8 and x3.data_ptr() % 16 == 0
+                 and scale.data_ptr() % 16 == 0 and shift.data_ptr() % 16 == 0)
+        if not fused:
+            return self.forward(rmsnorm_modulate_bf16(x, scale, shift, eps))
+        need = workspace_bytes(M, K)
+        if self._workspace is None or self._workspace.numel() < need or self._workspace.device != x.device:
+            self._workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        s_off = (M * K + 255) // 256 * 256
+        q = self._workspace[:M * K].view(torch.int8).view(M, K)
+        s = self._workspace[s_off:s_off + 4 * (M // BLOCK) * (K // BLOCK)].view(torch.float32)
+        rmsnorm_modulate_quantize_act(x3, scale, shift, eps, q, s.view(M // BLOCK, K // BLOCK))
+        out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
+        self.last_path = PATH_INT8
+        return out.view(*x.shape[:-1], N)
 
 
 class W8A8ProjectionGroup(torch.nn.Module):

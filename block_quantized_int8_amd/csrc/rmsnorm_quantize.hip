@@ -1,0 +1,216 @@
+// Modulated RMS normalization, alone and fused with the 128x128 block INT8
+// quantization of its result, for gfx950.
+//
+// The producer in front of a transformer block's linears: normalization
+// combined with timestep-dependent scale and shift (TurboT2VA paper,
+// architecture-aware inference stack, fused-kernels paragraph, which fuses
+// such memory-bound patterns); fused here with the activation quantization of
+// the next linear (the block rule: TurboDiffusion news article, bjdmk.com.cn,
+// 128x128 blocks for activations; TurboT2VA paper, W8A8 paragraph, scale =
+// max-abs / 127).  For row i = b*L + l of x [B*L, K]:
+//
+//   r_i  = fl32( 1 / sqrt(sum_k x_ik^2 / K + eps) )    (fp64, rounded once)
+//   y_ik = bf16( fl32(fl32(fl32(x_ik * r_i) * fl32(1 + scale[b,k])) + shift[b,k]) )
+//
+// every fl32 one IEEE fp32 operation (the library is built without
+// floating-point contraction), the bf16 rounding to nearest even.  The sum of
+// squares is taken in fp64 in this kernel's order (lane partials, then a
+// butterfly); a different order can move it by a few fp64 ulps, which changes
+// the fp32 r only when r lies within ~2^-50 of an fp32 rounding boundary.
+//
+// Three kernels: rms_rows (one wavefront per row, 16-byte loads, fp64
+// partial sums) writes r [B*L]; modulate_bf16 (one wavefront per row) writes
+// y; modulate_quantize (one workgroup per 128x128 block, the block
+// quantizer's structure) computes y in registers and emits its codes and
+// scale, so the bf16 y never reaches HBM.  The fused pair reads x twice
+// (the second time with nontemporal loads: it is x's last use) and writes
+// one byte per element; the unfused chain reads it twice and also writes and
+// re-reads the bf16 y.
+#include <math.h>
+
+#include "quant_math.h"
+#include "w8a8_internal.h"
+
+namespace w8a8 {
+namespace {
+
+constexpr int kRowWaves = 4;                        // rows (wavefronts) per workgroup
+constexpr int kBlkThreads = 256;
+constexpr int kChunksPerRow = kBlock * 2 / 16;      // 16-byte chunks per 128-column block row: 16
+constexpr int kRowsPerPass = kBlkThreads / kChunksPerRow;  // 16
+constexpr int kPasses = kBlock / kRowsPerPass;      // 8
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
+}
+
+__device__ __forceinline__ float modulate(float x, float r, float s, float h) {
+    const float t = x * r;
+    const float one_s = 1.0f + s;
+    const float u = t * one_s;
+    return u + h;
+}
+
+// Two packed bf16 (x, scale, shift words) -> two packed bf16 of y.
+__device__ __forceinline__ uint32_t modulate_word(uint32_t xw, uint32_t sw, uint32_t hw, float r) {
+    const float y0 = modulate(lo_bf16(xw), r, lo_bf16(sw), lo_bf16(hw));
+    const float y1 = modulate(hi_bf16(xw), r, hi_bf16(sw), hi_bf16(hw));
+    return bf16_bits(y0) | (bf16_bits(y1) << 16);
+}
+
+__device__ __forceinline__ u32x4 modulate_chunk(u32x4 x, u32x4 s, u32x4 h, float r) {
+    return u32x4{modulate_word(x.x, s.x, h.x, r), modulate_word(x.y, s.y, h.y, r),
+                 modulate_word(x.z, s.z, h.z, r), modulate_word(x.w, s.w, h.w, r)};
+}
+
+__device__ __forceinline__ double sq_chunk(u32x4 w) {
+    double a = 0.0;
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double l = (double)lo_bf16(v[i]), h = (double)hi_bf16(v[i]);
+        a += l * l;
+        a += h * h;
+    }
+    return a;
+}
+
+__global__ __launch_bounds__(64 * kRowWaves) void rms_rows_kernel(const uint16_t *__restrict__ x, int64_t rows,
+                                                                  int64_t K, double eps, float *__restrict__ r) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;  // whole wavefront leaves together
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + row * K);
+    const int64_t chunks = K / 8;
+    double acc = 0.0;
+    int64_t c = lane;
+    for (; c + 3 * 64 < chunks; c += 4 * 64) {  // four loads in flight per lane
+        const u32x4 a = src[c], b = src[c + 64], d = src[c + 128], e = src[c + 192];
+        acc += sq_chunk(a);
+        acc += sq_chunk(b);
+        acc += sq_chunk(d);
+        acc += sq_chunk(e);
+    }
+    for (; c < chunks; c += 64) acc += sq_chunk(src[c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) r[row] = (float)(1.0 / sqrt(acc / (double)K + eps));
+}
+
+// y for one row per wavefront.
+__global__ __launch_bounds__(64 * kRowWaves) void modulate_bf16_kernel(const uint16_t *__restrict__ x,
+                                                                       const float *__restrict__ r, int64_t rows,
+                                                                       int64_t L, int64_t K,
+                                                                       const uint16_t *__restrict__ scale,
+                                                                       const uint16_t *__restrict__ shift,
+                                                                       uint16_t *__restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int64_t b = row / L;
+    const float rr = r[row];
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + row * K);
+    const u32x4 *sc = reinterpret_cast<const u32x4 *>(scale + b * K);
+    const u32x4 *sh = reinterpret_cast<const u32x4 *>(shift + b * K);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(y + row * K);
+    const int64_t chunks = K / 8;
+    for (int64_t c = lane; c < chunks; c += 64) dst[c] = modulate_chunk(src[c], sc[c], sh[c], rr);
+}
+
+// One workgroup per 128x128 block of y: each thread holds 64 values (8
+// chunks of 8, rows r0 + 16p), computes them from x, its rows' r and their
+// batch entries' scale and shift, then quantizes them as the block quantizer
+// does (absmax on the magnitude bits, wavefront shuffles, LDS across the 4
+// wavefronts, one correctly rounded division per element).
+__global__ __launch_bounds__(kBlkThreads) void modulate_quantize_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ r, uint32_t L, int64_t K, int64_t col_blocks,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ shift, int8_t *__restrict__ q,
+    float *__restrict__ s) {
+    __shared__ uint32_t red[kBlkThreads / 64];
+    const int64_t tile = blockIdx.x;
+    const int64_t rb = tile / col_blocks, cb = tile - rb * col_blocks;
+    const int t = threadIdx.x;
+    const int chunk = t % kChunksPerRow, r0 = t / kChunksPerRow;
+    const int64_t row0 = rb * kBlock + r0;
+    const int64_t col = cb * kBlock + chunk * 8;
+
+    u32x4 v[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+        v[p] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(x + (row0 + (int64_t)p * kRowsPerPass) * K + col));
+    uint32_t m = 0;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int64_t row = row0 + (int64_t)p * kRowsPerPass;
+        const uint32_t b = (uint32_t)row / L;  // rows < 2^31 (checked by the caller)
+        const u32x4 sc = *reinterpret_cast<const u32x4 *>(scale + (int64_t)b * K + col);
+        const u32x4 sh = *reinterpret_cast<const u32x4 *>(shift + (int64_t)b * K + col);
+        v[p] = modulate_chunk(v[p], sc, sh, r[row]);
+        m = max(m, chunk_absmax_bits(v[p]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+
+    const float a = __uint_as_float(m << 16);
+    const float sc = a / 127.0f;  // IEEE division, correctly rounded
+    if (t == 0) s[tile] = sc;
+    int8_t *dst = q + row0 * K + col;
+    if (m == 0) {
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p)
+            *reinterpret_cast<u32x2 *>(dst + (int64_t)p * kRowsPerPass * K) = u32x2{0u, 0u};
+        return;
+    }
+    if (sc < kTinyScale) {
+        const float f = kPrescale, ss = sc * f, rcp = 1.0f / ss;
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p)
+            *reinterpret_cast<u32x2 *>(dst + (int64_t)p * kRowsPerPass * K) = code_chunk<true>(v[p], f, ss, rcp);
+    } else {
+        const float rcp = 1.0f / sc;
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p)
+            *reinterpret_cast<u32x2 *>(dst + (int64_t)p * kRowsPerPass * K) = code_chunk<false>(v[p], 1.0f, sc, rcp);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rms_rows(const uint16_t *x, int64_t rows, int64_t K, double eps, float *r, hipStream_t stream) {
+    const int64_t groups = (rows + kRowWaves - 1) / kRowWaves;
+    if (groups <= 0) return hipSuccess;
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    rms_rows_kernel<<<dim3((unsigned)groups), dim3(64 * kRowWaves), 0, stream>>>(x, rows, K, eps, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_modulate_bf16(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
+                                const uint16_t *scale, const uint16_t *shift, uint16_t *y, hipStream_t stream) {
+    const int64_t groups = (rows + kRowWaves - 1) / kRowWaves;
+    if (groups <= 0) return hipSuccess;
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    modulate_bf16_kernel<<<dim3((unsigned)groups), dim3(64 * kRowWaves), 0, stream>>>(x, r, rows, L, K, scale,
+                                                                                      shift, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_modulate_quantize(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
+                                    const uint16_t *scale, const uint16_t *shift, int8_t *q, float *s,
+                                    hipStream_t stream) {
+    const int64_t col_blocks = K / kBlock;
+    const int64_t tiles = (rows / kBlock) * col_blocks;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF || rows > 0x7FFFFFFF || L > 0x7FFFFFFF) return hipErrorInvalidValue;
+    modulate_quantize_kernel<<<dim3((unsigned)tiles), dim3(kBlkThreads), 0, stream>>>(
+        x, r, (uint32_t)L, K, col_blocks, scale, shift, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8

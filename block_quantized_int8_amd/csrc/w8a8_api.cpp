@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "w8a8_internal.h"
 
 namespace {
@@ -43,6 +45,18 @@ int quantize_strict(const void *x, int64_t R, int64_t C, int8_t *q, float *s, hi
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return W8A8_ERR_UNSUPPORTED;
     if (!is_device_ptr(x) || !is_device_ptr(q) || !is_device_ptr(s)) return W8A8_ERR_INVALID_ARG;
     return hip_status(w8a8::launch_quantize_block(static_cast<const uint16_t *>(x), R, C, q, s, stream));
+}
+
+// Shared checks of the two modulated-RMSNorm entry points (x, scale, shift,
+// r: device pointers; eps > 0 and finite).
+int rmsnorm_args(const void *x, int64_t B, int64_t L, int64_t K, const void *scale, const void *shift, double eps,
+                 const float *r_ws) {
+    if (!x || !scale || !shift || !r_ws || B <= 0 || L <= 0 || K <= 0 || !(eps > 0.0) || !std::isfinite(eps))
+        return W8A8_ERR_INVALID_ARG;
+    if (B > INT64_MAX / L || B * L > INT32_MAX) return W8A8_ERR_UNSUPPORTED;
+    if (K % 8 || !aligned(x, 16) || !aligned(scale, 16) || !aligned(shift, 16) || !aligned(r_ws, 4))
+        return W8A8_ERR_UNSUPPORTED;
+    return W8A8_OK;
 }
 
 }  // namespace
@@ -230,6 +244,40 @@ int w8a8_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_
     if (B > INT32_MAX / H || B * H > INT32_MAX / nblk) return W8A8_ERR_UNSUPPORTED;
     if (!is_device_ptr(x_bf16) || !is_device_ptr(q) || !is_device_ptr(s)) return W8A8_ERR_INVALID_ARG;
     return hip_status(w8a8::launch_quantize_qk(static_cast<const uint16_t *>(x_bf16), B, L, H, D, ld, q, s, stream));
+}
+
+int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                               const void *shift_bf16, double eps, float *r_ws, void *y_bf16, hipStream_t stream) {
+    const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, r_ws);
+    if (st != W8A8_OK) return st;
+    if (!y_bf16) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(y_bf16, 16)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(scale_bf16) || !is_device_ptr(shift_bf16) || !is_device_ptr(r_ws) ||
+        !is_device_ptr(y_bf16))
+        return W8A8_ERR_INVALID_ARG;
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    hipError_t e = w8a8::launch_rms_rows(x, B * L, K, eps, r_ws, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(w8a8::launch_modulate_bf16(x, r_ws, B * L, L, K, static_cast<const uint16_t *>(scale_bf16),
+                                                 static_cast<const uint16_t *>(shift_bf16),
+                                                 static_cast<uint16_t *>(y_bf16), stream));
+}
+
+int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                       const void *shift_bf16, double eps, float *r_ws, int8_t *qx, float *sx,
+                                       hipStream_t stream) {
+    const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, r_ws);
+    if (st != W8A8_OK) return st;
+    if (!qx || !sx) return W8A8_ERR_INVALID_ARG;
+    if (!mult128(B * L) || !mult128(K) || !aligned(qx, 16) || !aligned(sx, 4)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(scale_bf16) || !is_device_ptr(shift_bf16) || !is_device_ptr(r_ws) ||
+        !is_device_ptr(qx) || !is_device_ptr(sx))
+        return W8A8_ERR_INVALID_ARG;
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    hipError_t e = w8a8::launch_rms_rows(x, B * L, K, eps, r_ws, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(w8a8::launch_modulate_quantize(x, r_ws, B * L, L, K, static_cast<const uint16_t *>(scale_bf16),
+                                                     static_cast<const uint16_t *>(shift_bf16), qx, sx, stream));
 }
 
 const char *w8a8_status_string(int status) {

@@ -37,6 +37,15 @@ hipError_t launch_gelu_quantize_block(const uint16_t *y, int64_t rows, int64_t c
 hipError_t launch_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
                               int8_t *q, float *s, hipStream_t stream);
 
+// Modulated RMS normalization: r [rows] (fp32), y bf16, and y fused with the
+// 128x128 block quantization (rows and K multiples of 128, rows < 2^31).
+hipError_t launch_rms_rows(const uint16_t *x, int64_t rows, int64_t K, double eps, float *r, hipStream_t stream);
+hipError_t launch_modulate_bf16(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
+                                const uint16_t *scale, const uint16_t *shift, uint16_t *y, hipStream_t stream);
+hipError_t launch_modulate_quantize(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
+                                    const uint16_t *scale, const uint16_t *shift, int8_t *q, float *s,
+                                    hipStream_t stream);
+
 // bf16 fallback on the 256x256-tile kernel: x, w, y 16-byte aligned, K % 64 == 0,
 // K <= 2^21, N % 128 == 0, any M >= 1; bias 8-byte aligned or null.
 hipError_t launch_gemm_bf16_tiled(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M,

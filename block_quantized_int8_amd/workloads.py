@@ -23,6 +23,12 @@ these transformer-linear shapes stand in for them:
           only), 32 heads of 128; N(0, 1.28^2) with 1% of the key's channels
           x10 (heavy tails); ``l``/``heads``/``d`` select other (e.g. short,
           ragged audio) sequences
+* ``block_hidden``  a transformer block's hidden state with its modulation,
+          the input of the fused modulated-RMSNorm + quantize producer, seed 8:
+          x [b*l, k] ~ N(0, 2^2) with 1% of channels x10 (massive activations),
+          scale and shift [b, k] ~ N(0, 0.3^2) (per batch entry, as timestep
+          modulation is); default b = 4, l = 8192, k = 4096 (32768 rows, the
+          attention-projection input)
 * ``mlp_hidden``  stand-in for the MLP pair's up-projection output (the input
           of the fused GELU + quantize producer), 32768 x 16384, seed 5:
           N(0, 1.28^2), the spread of the MLP pair's up projection (sqrt(4096) * 0.02)
@@ -155,3 +161,17 @@ def attention_qk(l: int = 28672, heads: int = 32, d: int = 128, seed: int = 6):
     ch = _outlier_channels(rng, heads * d, 0.01)
     k[:, ch] *= np.float32(10.0)
     return {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k)}
+
+
+def block_hidden(b: int = 4, l: int = 8192, k: int = 4096, seed: int = 8):
+    """{"x": bf16 [b*l, k], "scale": bf16 [b, k], "shift": bf16 [b, k], "L": l}."""
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (b * l, k), 2.0)
+    scale = _normal(rng, (b, k), 0.3)
+    shift = _normal(rng, (b, k), 0.3)
+    ch = _outlier_channels(rng, k, 0.01)
+    x[:, ch] *= np.float32(10.0)
+    out = np.empty((b * l, k), np.uint16)
+    for r in range(0, b * l, 2048):  # bounded temporaries; same bits as one call
+        out[r:r + 2048] = f32_to_bf16_bits(x[r:r + 2048])
+    return {"x": out, "scale": f32_to_bf16_bits(scale), "shift": f32_to_bf16_bits(shift), "L": l}

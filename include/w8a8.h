@@ -228,6 +228,39 @@ int w8a8_gelu_quantize_act(const void *y_bf16, int64_t M, int64_t K, int8_t *qx,
                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The other producer the TurboT2VA paper fuses (architecture-aware inference
+ * stack, fused-kernels paragraph): RMS normalization combined with a
+ * timestep-dependent scale and shift, the input of a transformer block's
+ * projections.  For row i = b*L + l of x_bf16 [B*L, K] (L tokens per batch
+ * entry b; scale_bf16 and shift_bf16 are [B, K]):
+ *   r_i  = fl32( 1 / sqrt(sum_k x_ik^2 / K + eps) )   (fp64, rounded once),
+ *   y_ik = bf16( fl32(fl32(fl32(x_ik * r_i) * fl32(1 + scale[b,k])) + shift[b,k]) )
+ * each fl32 one IEEE fp32 operation, bf16 rounding to nearest even.  The sum
+ * of squares is an fp64 sum in the kernel's order; another order can move
+ * it by a few fp64 ulps, which changes r only when r lies within ~2^-50 of
+ * an fp32 rounding boundary.  r_ws is a caller-provided workspace of B*L
+ * floats that receives r.  eps must be finite and > 0, inputs finite;
+ * B*L < 2^31.  Errors: null pointers, sizes <= 0 or a bad eps ->
+ * W8A8_ERR_INVALID_ARG; K % 8 != 0, x, scale, shift (and y or qx) not
+ * 16-byte aligned or r_ws not 4-byte aligned -> W8A8_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+
+/* y_bf16 [B*L, K] = the modulated normalization of x (any B*L >= 1). */
+int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                               const void *shift_bf16, double eps, float *r_ws, void *y_bf16, hipStream_t stream);
+
+/*
+ * Fused producer + quantize: y as above, quantized by the block rule of
+ * w8a8_quantize_act into qx int8 [B*L, K] and sx fp32 [B*L/128, K/128]
+ * without ever being written (equal, bit for bit, to w8a8_quantize_act
+ * applied to w8a8_rmsnorm_modulate_bf16's output).  B*L and K must be
+ * multiples of 128 (else W8A8_ERR_UNSUPPORTED).
+ */
+int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                       const void *shift_bf16, double eps, float *r_ws, int8_t *qx, float *sx,
+                                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * INT8 query/key for the sparse attention (TurboT2VA paper, architecture-
  * aware inference stack, sparse-attention paragraph: query and key are
  * quantized to INT8, and the sequence-major tensors are rearranged into the

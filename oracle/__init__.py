@@ -48,10 +48,11 @@ def lib():
         L.oracle_quantize_rows.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_linear_postscale_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
         L.oracle_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
+        L.oracle_rmsnorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
         for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
                   "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
                   "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
-                  "oracle_quantize_qk"):
+                  "oracle_quantize_qk", "oracle_rmsnorm_modulate"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -196,3 +197,29 @@ def linear_postscale(qx, sx, qw, sw, bias=None, rows=None):
     _check(lib().oracle_linear_postscale_rows(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(b), M, N, K,
                                               _ptr(r), nr, _ptr(y)), "linear_postscale")
     return y
+
+
+def rmsnorm_modulate(x_bf16: np.ndarray, L: int, scale_bf16: np.ndarray, shift_bf16: np.ndarray,
+                     eps: float = 1e-6, want_r: bool = False):
+    """Modulated RMS normalization of x [B*L, K] (bf16 bits) with per-batch
+    scale and shift [B, K] -> y bf16 bits [B*L, K] (and r fp32 [B*L])."""
+    x = _c(x_bf16, np.uint16)
+    sc = _c(scale_bf16, np.uint16)
+    sh = _c(shift_bf16, np.uint16)
+    R, K = x.shape
+    if R % L:
+        raise ValueError("rows must be a multiple of L")
+    B = R // L
+    if sc.shape != (B, K) or sh.shape != (B, K):
+        raise ValueError("scale and shift must be [B, K]")
+    y = np.empty((R, K), np.uint16)
+    r = np.empty((R,), np.float32)
+    _check(lib().oracle_rmsnorm_modulate(_ptr(x), B, L, K, _ptr(sc), _ptr(sh), float(eps), _ptr(y), _ptr(r)),
+           "rmsnorm_modulate")
+    return (y, r) if want_r else y
+
+
+def rmsnorm_modulate_quantize_block(x_bf16, L, scale_bf16, shift_bf16, eps=1e-6):
+    """The fused producer's result: the modulated RMS normalization rounded to
+    bf16, then the 128x128 block quantization of that matrix -> (q, s)."""
+    return quantize_block(rmsnorm_modulate(x_bf16, L, scale_bf16, shift_bf16, eps))

@@ -26,6 +26,10 @@
  *   - INT8 query/key of the sparse attention, block rule over 128 tokens x
  *       head dim, rearranged sequence-major -> head-major: TurboT2VA paper,
  *       same section, sparse-attention paragraph.
+ *   - modulated RMS normalization (normalization combined with timestep-
+ *       dependent scale and shift), the producer of the projections' input:
+ *       TurboT2VA paper, same section, fused-kernels paragraph; the
+ *       formula's precision and order are this library's reading.
  *   - test-harness producer of the MLP-pair workload (not on the pages, which
  *       leave the MLP's activation open): exact GELU, x * Phi(x) (Hendrycks
  *       and Gimpel, "Gaussian Error Linear Units"), rounded once to bf16;
@@ -394,6 +398,48 @@ int oracle_gelu_bf16(const uint16_t *x, int64_t n, uint16_t *y) {
     for (int64_t i = 0; i < n; ++i) {
         double v = (double)oracle_bf16_to_f32(x[i]);
         y[i] = oracle_f64_to_bf16(0.5 * v * erfc(-v / sqrt(2.0)));
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------- modulated RMS normalization */
+
+/*
+ * Modulated RMS normalization of a bf16 activation, the producer in front of
+ * a transformer block's linears (TurboT2VA paper, architecture-aware
+ * inference stack, fused-kernels paragraph: normalization combined with
+ * modality- and timestep-dependent modulation; fused there, here fused with
+ * the 128x128 block quantization of the next linear's input).
+ * Row i = b*L + l of x [B*L, K] (L tokens per batch entry b):
+ *   S_i  = sum_k x_ik^2                          (fp64),
+ *   r_i  = fl32( 1 / sqrt(S_i / K + eps) )       (fp64, rounded once to fp32),
+ *   y_ik = bf16( fl32( fl32( fl32(x_ik * r_i) * fl32(1 + scale[b,k]) ) + shift[b,k] ) ),
+ * every fl32 one IEEE fp32 operation (no fused multiply-add), the bf16
+ * rounding to nearest even.  scale and shift are bf16 [B, K]; y is bf16
+ * [B*L, K]; r_out (nullable) receives r [B*L].  eps must be > 0, inputs
+ * finite.
+ */
+int oracle_rmsnorm_modulate(const uint16_t *x, int64_t B, int64_t L, int64_t K, const uint16_t *scale,
+                            const uint16_t *shift, double eps, uint16_t *y, float *r_out) {
+    if (!x || !scale || !shift || !y || B <= 0 || L <= 0 || K <= 0 || !(eps > 0.0)) return OR_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < B * L; ++i) {
+        const int64_t b = i / L;
+        const uint16_t *xr = x + i * K;
+        double S = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double v = (double)oracle_bf16_to_f32(xr[k]);
+            S += v * v;
+        }
+        const float r = (float)(1.0 / sqrt(S / (double)K + eps));
+        if (r_out) r_out[i] = r;
+        for (int64_t k = 0; k < K; ++k) {
+            const float t = oracle_bf16_to_f32(xr[k]) * r;
+            const float one_s = 1.0f + oracle_bf16_to_f32(scale[b * K + k]);
+            const float u = t * one_s;
+            const float v = u + oracle_bf16_to_f32(shift[b * K + k]);
+            y[i * K + k] = oracle_f64_to_bf16((double)v);
+        }
     }
     return OR_OK;
 }

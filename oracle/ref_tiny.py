@@ -183,3 +183,27 @@ def quantize_qk(x_bits: np.ndarray, B: int, L: int, H: int, D: int, ld: int):
                 s[b, h, j] = sc
                 q[b, h, j * BLOCK:j * BLOCK + blk.shape[0]] = _codes(blk, sc)
     return q, s
+
+
+# ------------------------------------------------ modulated RMS normalization
+
+def rmsnorm_modulate(x_bits: np.ndarray, L: int, scale_bits: np.ndarray, shift_bits: np.ndarray,
+                     eps: float = 1e-6) -> np.ndarray:
+    """Row i = b*L + l: r = fl32(1 / sqrt(sum_k x^2 / K + eps)) with the sum
+    taken exactly (math.fsum) and the rest in fp64; then per element, each
+    step one fp32 rounding: bf16(((x * r) * (1 + scale[b])) + shift[b])."""
+    x = bf16_to_f64(x_bits)
+    sc = bf16_to_f64(scale_bits).astype(np.float32)
+    sh = bf16_to_f64(shift_bits).astype(np.float32)
+    R, K = x.shape
+    y = np.zeros((R, K), np.uint16)
+    for i in range(R):
+        b = i // L
+        S = math.fsum(float(v) * float(v) for v in x[i])
+        r = np.float32(1.0 / math.sqrt(S / K + eps))
+        for k in range(K):
+            t = np.float32(np.float32(x[i, k]) * r)
+            u = np.float32(t * np.float32(np.float32(1.0) + sc[b, k]))
+            v = np.float32(u + sh[b, k])
+            y[i, k] = f64_to_bf16_bits(float(v))
+    return y

@@ -32,6 +32,11 @@ hipError_t launch_gemm_bf16_tiled(const uint16_t *, const uint16_t *, const uint
                                   uint16_t *, hipStream_t) { reached("gemm_bf16_tiled"); }
 hipError_t launch_gemm_bf16(const void *, int, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t, uint16_t *,
                             hipStream_t) { reached("gemm_bf16"); }
+hipError_t launch_rms_rows(const uint16_t *, int64_t, int64_t, double, float *, hipStream_t) { reached("rms_rows"); }
+hipError_t launch_modulate_bf16(const uint16_t *, const float *, int64_t, int64_t, int64_t, const uint16_t *,
+                                const uint16_t *, uint16_t *, hipStream_t) { reached("modulate_bf16"); }
+hipError_t launch_modulate_quantize(const uint16_t *, const float *, int64_t, int64_t, int64_t, const uint16_t *,
+                                    const uint16_t *, int8_t *, float *, hipStream_t) { reached("modulate_quantize"); }
 }  // namespace w8a8
 
 #define CHECK(cond)                                                                    \
@@ -100,6 +105,19 @@ int main() {
     CHECK(w8a8_quantize_qk(p, 1, 256, 2, 96, 192, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_quantize_qk(p, 1, 256, 2, 128, 255, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_quantize_qk(p, 1LL << 40, 256, 1LL << 20, 128, 1LL << 27, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    // modulated RMS normalization: eps, sizes, alignment, the fused path's block shape
+    CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, 0.0, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, -1e-6, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, __builtin_inf(), f, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 252, p, p, 1e-6, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rmsnorm_modulate_bf16(p, 0, 64, 256, p, p, 1e-6, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, static_cast<char *>(p) + 8, p, 1e-6, f, p, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rmsnorm_modulate_bf16(p, 1LL << 20, 1LL << 12, 256, p, p, 1e-6, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 100, 256, p, p, 1e-6, f, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 200, p, p, 1e-6, f, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 256, p, p, 1e-6, f, nullptr, f, nullptr) ==
+          W8A8_ERR_INVALID_ARG);
     std::printf("host sanitizer driver: ok\n");
     return 0;
 }

@@ -118,3 +118,19 @@ def test_host_decided_errors_producer_and_qk(L):
     assert L.w8a8_quantize_qk(fake, 1, 100, 2, 64, 132, fake, fake, null) == 2
     assert L.w8a8_quantize_qk(fake, 1, 0, 2, 64, 128, fake, fake, null) == 1
     assert L.w8a8_quantize_qk(ctypes.c_void_p(0x1008), 1, 100, 2, 64, 128, fake, fake, null) == 2
+
+
+def test_host_decided_errors_rmsnorm(L):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced
+    null = None
+    # eps must be finite and positive; sizes positive; K a multiple of 8
+    assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 64, 256, fake, fake, 0.0, fake, fake, null) == 1
+    assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 64, 256, fake, fake, float("nan"), fake, fake, null) == 1
+    assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 0, 256, fake, fake, 1e-6, fake, fake, null) == 1
+    assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 64, 252, fake, fake, 1e-6, fake, fake, null) == 2
+    assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 64, 256, fake, fake, 1e-6, null, fake, null) == 1
+    # fused: B*L and K multiples of 128
+    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 100, 256, fake, fake, 1e-6, fake, fake, fake, null) == 2
+    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 128, 192, fake, fake, 1e-6, fake, fake, fake, null) == 2
+    assert L.w8a8_rmsnorm_modulate_quantize_act(ctypes.c_void_p(0x1008), 2, 128, 256, fake, fake, 1e-6, fake, fake,
+                                                fake, null) == 2
