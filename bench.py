@@ -61,6 +61,10 @@ CPU_SAMPLE_BLOCKS = 256     # 128-row blocks of X the oracle processes (all 3276
 HM, HK = 32768, 16384
 PRODUCER_BYTES = HM * HK * 2 + HM * HK + (HM // 128) * (HK // 128) * 4   # read bf16, write int8 + scales
 GELU_BYTES = HM * HK * 2 * 2                                              # read and write bf16
+# transformer-block input for the modulated-RMSNorm producer: read bf16 x,
+# write int8 + block scales, read the [B, K] scale and shift
+RB, RL, RK = 4, 8192, 4096
+RMS_BYTES = RB * RL * RK * 3 + (RB * RL // 128) * (RK // 128) * 4 + 2 * RB * RK * 2
 # attention Q or K of one video self-attention: read bf16, write int8 + one scale per 128 tokens x head
 AL, AH, AD = 28672, 32, 128
 QK_BYTES = AL * AH * AD * 3 + AH * (AL // 128) * 4
@@ -187,6 +191,23 @@ def qk_buffers(dev):
     qq = torch.empty((AH, AL, AD), dtype=torch.int8, device=dev)
     sq = torch.empty((AH, AL // 128), dtype=torch.float32, device=dev)
     return qkv, qq, sq
+
+
+def rms_buffers(dev):
+    """A transformer block's hidden state (B = 4 x L = 8192 tokens x 4096)
+    with its modulation, and the producer's outputs."""
+    import numpy as np
+    import torch
+    from block_quantized_int8_amd.workloads import block_hidden
+    t0 = time.perf_counter()
+    d = block_hidden(RB, RL, RK)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    xr, sc, sh = to(d["x"]).view(RB, RL, RK), to(d["scale"]), to(d["shift"])
+    log(f"block hidden state ready ({time.perf_counter() - t0:.1f} s): {tuple(xr.shape)}")
+    yr = torch.empty_like(xr)
+    q = torch.empty((RB * RL, RK), dtype=torch.int8, device=dev)
+    s = torch.empty((RB * RL // 128, RK // 128), dtype=torch.float32, device=dev)
+    return xr, sc, sh, yr, q, s
 
 
 def producer_buffers(w8a8, dev):
@@ -460,6 +481,30 @@ def main():
         f"({PRODUCER_BYTES / prod_us['fused'] / 1e3:.0f} GB/s) vs gelu {prod_us['gelu']:.1f} + "
         f"quantize {prod_us['quantize']:.1f} us")
 
+    # producer A/B on a transformer block's input: modulated RMSNorm fused
+    # with the block quantization vs the normalization then the quantizer
+    xr, rsc, rsh, yr, rq, rs = rms_buffers(dev)
+    w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)    # untimed first launches
+    w8a8.rmsnorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)
+    torch.cuda.synchronize()
+    rt = {"fused": [], "norm": [], "quantize": []}
+    for i in range(args.steps):
+        for key, fn in (("fused", lambda: w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)),
+                        ("norm", lambda: w8a8.rmsnorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)),
+                        ("quantize", lambda: w8a8.quantize_act(yr.view(RB * RL, RK), rq, rs))):
+            flush.amax()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            rt[key].append((a, b))
+    torch.cuda.synchronize()
+    rms_us = {k: sum(a.elapsed_time(b) for a, b in v) / args.steps * 1e3 for k, v in rt.items()}
+    del xr, rsc, rsh, yr, rq, rs
+    log(f"RMSNorm producer A/B ({RB}x{RL}x{RK}): fused {rms_us['fused']:.1f} us "
+        f"({RMS_BYTES / rms_us['fused'] / 1e3:.0f} GB/s algorithmic) vs norm {rms_us['norm']:.1f} + "
+        f"quantize {rms_us['quantize']:.1f} us")
+
     # A/B: the post-scale form (per-row / per-channel scales applied once,
     # INT32 over all of K) on the same inputs and shape
     qwp, swp = w8a8.quantize_rows(w)
@@ -559,6 +604,17 @@ def main():
                         "us": round(qk_us, 2), "gbs": round(QK_BYTES / qk_us / 1e3, 1),
                         "frac_of_hbm": round(QK_BYTES / qk_us / 1e3 / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": QK_BYTES},
+        "rmsnorm_producer_ab": {"note": "transformer-block input: modulated RMSNorm fused with the 128x128 "
+                                        "block quantize vs the normalization then the quantizer (not part of a "
+                                        "step); the fused entry reads x twice (row norms, then the blocks)",
+                                "shape": [RB, RL, RK],
+                                "fused_us": round(rms_us["fused"], 2),
+                                "fused_gbs_algorithmic": round(RMS_BYTES / rms_us["fused"] / 1e3, 1),
+                                "fused_frac_of_hbm": round(RMS_BYTES / rms_us["fused"] / 1e3 / PEAK_HBM_GBS, 4),
+                                "algorithmic_bytes": RMS_BYTES,
+                                "unfused_norm_us": round(rms_us["norm"], 2),
+                                "unfused_quantize_us": round(rms_us["quantize"], 2),
+                                "speedup": round((rms_us["norm"] + rms_us["quantize"]) / rms_us["fused"], 3)},
         "producer_ab": {"note": "MLP producer: exact GELU + 128x128 block quantize of the hidden "
                                 "activation, fused vs GELU then quantize (not part of a step)",
                         "shape": [HM, HK],

@@ -108,8 +108,9 @@ __global__ __launch_bounds__(64 * kRowWaves) void modulate_bf16_kernel(const uin
                                                                        const uint16_t *__restrict__ shift,
                                                                        uint16_t *__restrict__ y) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    // last rows first, as in modulate_quantize_kernel
+    const int64_t row = rows - 1 - ((int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6));
+    if (row < 0) return;
     const int64_t b = row / L;
     const float rr = r[row];
     const u32x4 *src = reinterpret_cast<const u32x4 *>(x + row * K);
@@ -130,7 +131,9 @@ __global__ __launch_bounds__(kBlkThreads) void modulate_quantize_kernel(
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ shift, int8_t *__restrict__ q,
     float *__restrict__ s) {
     __shared__ uint32_t red[kBlkThreads / 64];
-    const int64_t tile = blockIdx.x;
+    // last rows first: the row-norm pass has just streamed x through the
+    // last-level cache, whose most recent lines are the last rows
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t rb = tile / col_blocks, cb = tile - rb * col_blocks;
     const int t = threadIdx.x;
     const int chunk = t % kChunksPerRow, r0 = t / kChunksPerRow;
@@ -143,14 +146,27 @@ __global__ __launch_bounds__(kBlkThreads) void modulate_quantize_kernel(
         v[p] = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4 *>(x + (row0 + (int64_t)p * kRowsPerPass) * K + col));
     uint32_t m = 0;
+    // rows < 2^31 (checked by the caller), so 32-bit division suffices
+    const uint32_t b_first = (uint32_t)(rb * kBlock) / L, b_last = (uint32_t)(rb * kBlock + kBlock - 1) / L;
+    if (b_first == b_last) {
+        // the whole block belongs to one batch entry: one scale/shift chunk per thread
+        const u32x4 sc = *reinterpret_cast<const u32x4 *>(scale + (int64_t)b_first * K + col);
+        const u32x4 sh = *reinterpret_cast<const u32x4 *>(shift + (int64_t)b_first * K + col);
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-        const int64_t row = row0 + (int64_t)p * kRowsPerPass;
-        const uint32_t b = (uint32_t)row / L;  // rows < 2^31 (checked by the caller)
-        const u32x4 sc = *reinterpret_cast<const u32x4 *>(scale + (int64_t)b * K + col);
-        const u32x4 sh = *reinterpret_cast<const u32x4 *>(shift + (int64_t)b * K + col);
-        v[p] = modulate_chunk(v[p], sc, sh, r[row]);
-        m = max(m, chunk_absmax_bits(v[p]));
+        for (int p = 0; p < kPasses; ++p) {
+            v[p] = modulate_chunk(v[p], sc, sh, r[row0 + (int64_t)p * kRowsPerPass]);
+            m = max(m, chunk_absmax_bits(v[p]));
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            const int64_t row = row0 + (int64_t)p * kRowsPerPass;
+            const uint32_t b = (uint32_t)row / L;
+            const u32x4 sc = *reinterpret_cast<const u32x4 *>(scale + (int64_t)b * K + col);
+            const u32x4 sh = *reinterpret_cast<const u32x4 *>(shift + (int64_t)b * K + col);
+            v[p] = modulate_chunk(v[p], sc, sh, r[row]);
+            m = max(m, chunk_absmax_bits(v[p]));
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
