@@ -229,7 +229,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk"], default=None)
+    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "rms"],
+                    default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -280,6 +281,14 @@ def main():
             w8a8.quantize_qk(qkv[:, :AH * AD], AH, qq, sq)
         torch.cuda.synchronize()
         log(f"--only qk: {args.steps} launches done")
+        return
+
+    if args.only == "rms":
+        xr, rsc, rsh, yr, rq, rs = rms_buffers(dev)
+        for _ in range(args.steps):
+            w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)
+        torch.cuda.synchronize()
+        log(f"--only rms: {args.steps} launches done")
         return
 
     if args.only in ("gelu_quant", "gelu"):
