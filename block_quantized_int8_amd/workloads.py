@@ -175,3 +175,29 @@ def block_hidden(b: int = 4, l: int = 8192, k: int = 4096, seed: int = 8):
     for r in range(0, b * l, 2048):  # bounded temporaries; same bits as one call
         out[r:r + 2048] = f32_to_bf16_bits(x[r:r + 2048])
     return {"x": out, "scale": f32_to_bf16_bits(scale), "shift": f32_to_bf16_bits(shift), "L": l}
+
+
+def rope_tables(l: int, d: int, grid=None, base: float = 10000.0):
+    """(cos, sin): fp32 [l, d/2] tables of rotary angles, one row per token.
+
+    Inputs of the rotary embedding, not part of it: angle(p, i) = p *
+    base^(-i / n) for pair i of a group of n pairs, in fp64, then cos and sin
+    rounded once to fp32.  With ``grid = (f, h, w)`` (f*h*w = l tokens in
+    frame, row, column order) the d/2 pairs are split into three groups
+    (the first takes the remainder) driven by the token's frame, row and
+    column index, as video transformers place tokens; else one group driven
+    by the position l.  No random numbers are drawn.
+    """
+    half = d // 2
+    pos = np.arange(l, dtype=np.float64)
+    if grid is None:
+        groups = [(pos, half)]
+    else:
+        f, h, w = grid
+        if f * h * w != l:
+            raise ValueError("grid does not cover l tokens")
+        n_hw = half // 3
+        groups = [(pos // (h * w), half - 2 * n_hw), ((pos // w) % h, n_hw), (pos % w, n_hw)]
+    ang = np.concatenate([p[:, None] * base ** (-np.arange(n, dtype=np.float64) / n)[None, :] for p, n in groups],
+                         axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)

@@ -49,10 +49,11 @@ def lib():
         L.oracle_linear_postscale_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
         L.oracle_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
         L.oracle_rmsnorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
+        L.oracle_rope.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
         for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
                   "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
                   "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
-                  "oracle_quantize_qk", "oracle_rmsnorm_modulate"):
+                  "oracle_quantize_qk", "oracle_rmsnorm_modulate", "oracle_rope"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -223,3 +224,23 @@ def rmsnorm_modulate_quantize_block(x_bf16, L, scale_bf16, shift_bf16, eps=1e-6)
     """The fused producer's result: the modulated RMS normalization rounded to
     bf16, then the 128x128 block quantization of that matrix -> (q, s)."""
     return quantize_block(rmsnorm_modulate(x_bf16, L, scale_bf16, shift_bf16, eps))
+
+
+def rope(x_bf16: np.ndarray, B: int, L: int, H: int, D: int, ld: int, cos_t: np.ndarray, sin_t: np.ndarray):
+    """Split-halves rotary embedding of sequence-major Q or K (rows of ``ld``
+    bf16, element (b, l, h, d) at row b*L + l, column h*D + d) with fp32
+    tables [L, D/2] -> bf16 [B*L, H*D] (contiguous, sequence-major)."""
+    x = _c(x_bf16, np.uint16)
+    c = _c(cos_t, np.float32)
+    s = _c(sin_t, np.float32)
+    if x.size != B * L * ld or c.shape != (L, D // 2) or s.shape != (L, D // 2):
+        raise ValueError("shapes: x [B*L, ld], tables [L, D/2]")
+    y = np.empty((B * L, H * D), np.uint16)
+    _check(lib().oracle_rope(_ptr(x), B, L, H, D, ld, _ptr(c), _ptr(s), _ptr(y)), "rope")
+    return y
+
+
+def rope_quantize_qk(x_bf16, B, L, H, D, ld, cos_t, sin_t):
+    """The fused Q/K producer's result: the rotary embedding rounded to bf16,
+    then quantize_qk of that (contiguous) result -> (q [B, H, L, D], s)."""
+    return quantize_qk(rope(x_bf16, B, L, H, D, ld, cos_t, sin_t), B, L, H, D, H * D)

@@ -26,6 +26,9 @@
  *   - INT8 query/key of the sparse attention, block rule over 128 tokens x
  *       head dim, rearranged sequence-major -> head-major: TurboT2VA paper,
  *       same section, sparse-attention paragraph.
+ *   - rotary position embedding in the split-halves form on Q and K ahead
+ *       of their INT8 quantization: same section, fused-kernels paragraph
+ *       (split rotary embeddings among the fused patterns).
  *   - modulated RMS normalization (normalization combined with timestep-
  *       dependent scale and shift), the producer of the projections' input:
  *       TurboT2VA paper, same section, fused-kernels paragraph; the
@@ -360,6 +363,40 @@ int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64
                     out = (int8_t)t;
                 }
                 q[(bh * L + l) * D + d] = out;
+            }
+    }
+    return OR_OK;
+}
+
+/*
+ * Rotary position embedding in the split-halves form on sequence-major
+ * Q or K (TurboT2VA paper, architecture-aware inference stack, fused-kernels
+ * paragraph: split rotary embeddings among the fused patterns), before the
+ * INT8 quantization of the sparse attention's inputs.  For element
+ * (b, l, h, d) at x[(b*L + l)*ld + h*D + d], with half = D/2, d < half,
+ * c = cos_t[l*half + d] and s = sin_t[l*half + d] (fp32, shared by every
+ * batch entry and head):
+ *   y(d)        = bf16( fl32( fl32(x(d) * c) - fl32(x(d + half) * s) ) )
+ *   y(d + half) = bf16( fl32( fl32(x(d + half) * c) + fl32(x(d) * s) ) )
+ * each fl32 one IEEE fp32 operation, bf16 to nearest even.  y is
+ * sequence-major and contiguous: y[(b*L + l)*H*D + h*D + d].  D even.
+ */
+int oracle_rope(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
+                const float *sin_t, uint16_t *y) {
+    if (!x || !cos_t || !sin_t || !y || B <= 0 || L <= 0 || H <= 0 || D <= 0 || D % 2 || ld < H * D)
+        return OR_ERR_ARG;
+    const int64_t half = D / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < B * L; ++row) {
+        const int64_t l = row % L;
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t d = 0; d < half; ++d) {
+                const float x1 = oracle_bf16_to_f32(x[row * ld + h * D + d]);
+                const float x2 = oracle_bf16_to_f32(x[row * ld + h * D + d + half]);
+                const float c = cos_t[l * half + d], s = sin_t[l * half + d];
+                const float a = x1 * c, b = x2 * s, e = x2 * c, f = x1 * s;
+                y[row * H * D + h * D + d] = oracle_f64_to_bf16((double)(a - b));
+                y[row * H * D + h * D + d + half] = oracle_f64_to_bf16((double)(e + f));
             }
     }
     return OR_OK;

@@ -20,7 +20,9 @@ the definitions:
   per-output-channel max(max-abs, 1e-4) / 127, integer sum over all of K,
   scales and bias once at the end);
 * INT8 attention Q/K (TurboT2VA paper, sparse-attention paragraph): the
-  block rule over 128 tokens x the head dimension, per batch and head.
+  block rule over 128 tokens x the head dimension, per batch and head;
+* the modulated RMS normalization and the split-halves rotary embedding
+  (TurboT2VA paper, fused-kernels paragraph).
 
 Everything is O(M*N*K) Python-level numpy on small arrays: use it on
 inputs of a few hundred rows at most.
@@ -206,4 +208,26 @@ def rmsnorm_modulate(x_bits: np.ndarray, L: int, scale_bits: np.ndarray, shift_b
             u = np.float32(t * np.float32(np.float32(1.0) + sc[b, k]))
             v = np.float32(u + sh[b, k])
             y[i, k] = f64_to_bf16_bits(float(v))
+    return y
+
+
+# ------------------------------------------------------ split rotary embedding
+
+def rope(x_bits: np.ndarray, B: int, L: int, H: int, D: int, ld: int, cos_t: np.ndarray, sin_t: np.ndarray):
+    """Pairs (d, d + D/2) of each head rotated by the token's table angle,
+    each product and sum one fp32 rounding, the result rounded to bf16."""
+    x = bf16_to_f64(np.asarray(x_bits, np.uint16).reshape(B * L, ld)).astype(np.float32)
+    half = D // 2
+    y = np.zeros((B * L, H * D), np.uint16)
+    for row in range(B * L):
+        l = row % L
+        c = np.asarray(cos_t, np.float32)[l]
+        s = np.asarray(sin_t, np.float32)[l]
+        for h in range(H):
+            x1 = x[row, h * D:h * D + half]
+            x2 = x[row, h * D + half:h * D + D]
+            lo = (x1 * c).astype(np.float32) - (x2 * s).astype(np.float32)
+            hi = (x2 * c).astype(np.float32) + (x1 * s).astype(np.float32)
+            y[row, h * D:h * D + half] = f64_to_bf16_array(lo.astype(np.float32).astype(np.float64))
+            y[row, h * D + half:h * D + D] = f64_to_bf16_array(hi.astype(np.float32).astype(np.float64))
     return y

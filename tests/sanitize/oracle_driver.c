@@ -24,6 +24,10 @@ int oracle_linear_postscale_rows(const int8_t *qx, const float *sx, const int8_t
 int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, int8_t *q,
                        float *s);
 int oracle_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight);
+int oracle_rope(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
+                const float *sin_t, uint16_t *y);
+int oracle_rmsnorm_modulate(const uint16_t *x, int64_t B, int64_t L, int64_t K, const uint16_t *scale,
+                            const uint16_t *shift, double eps, uint16_t *y, float *r_out);
 int oracle_gelu_bf16(const uint16_t *x, int64_t n, uint16_t *y);
 uint16_t oracle_f64_to_bf16(double v);
 double oracle_fp16_to_f64(uint16_t h);
@@ -91,6 +95,23 @@ int main(void) {
     CHECK(oracle_quantize_qk(qkx, B, L, H, D, ld, qq, qs) == 0);
     CHECK(oracle_quantize_qk(qkx, B, L, H, D, H * D - 1, qq, qs) != 0);
 
+    /* split rotary embedding on the same padded rows */
+    float *rc = xmalloc(sizeof(float) * L * (D / 2)), *rs = xmalloc(sizeof(float) * L * (D / 2));
+    for (int64_t i = 0; i < L * (D / 2); ++i) {
+        rc[i] = (float)((int)(next_u32() % 2001) - 1000) / 1000.0f;
+        rs[i] = (float)((int)(next_u32() % 2001) - 1000) / 1000.0f;
+    }
+    uint16_t *ry = xmalloc(sizeof(uint16_t) * B * L * H * D);
+    CHECK(oracle_rope(qkx, B, L, H, D, ld, rc, rs, ry) == 0);
+    CHECK(oracle_rope(qkx, B, L, H, D - 1, ld, rc, rs, ry) != 0);      /* odd head dimension */
+    CHECK(oracle_rope(qkx, B, L, H, D, H * D - 1, rc, rs, ry) != 0);
+
+    /* modulated RMS normalization, with its r */
+    uint16_t *nsc = bf16_buf(2 * K), *nsh = bf16_buf(2 * K), *ny = xmalloc(sizeof(uint16_t) * M * K);
+    float *nr = xmalloc(sizeof(float) * M);
+    CHECK(oracle_rmsnorm_modulate(x, 2, M / 2, K, nsc, nsh, 1e-6, ny, nr) == 0);
+    CHECK(oracle_rmsnorm_modulate(x, 2, M / 2, K, nsc, nsh, 1e-6, ny, NULL) == 0);
+
     /* GELU over every bf16 pattern (NaN/Inf included: defined output, no UB) */
     uint16_t *gin = xmalloc(sizeof(uint16_t) * 65536), *gout = xmalloc(sizeof(uint16_t) * 65536);
     for (int i = 0; i < 65536; ++i) gin[i] = (uint16_t)i;
@@ -105,6 +126,7 @@ int main(void) {
 
     free(x); free(w); free(b); free(qx); free(qw); free(sx); free(sw); free(p); free(y); free(y64); free(yall);
     free(fx); free(fw); free(fy); free(fx32); free(rsx); free(rsw); free(qkx); free(qq); free(qs); free(gin); free(gout);
+    free(rc); free(rs); free(ry); free(nsc); free(nsh); free(ny); free(nr);
     printf("oracle sanitizer driver: ok\n");
     return 0;
 }
