@@ -26,7 +26,9 @@ Projections sharing one input (Q/K/V, or cross-attention K/V):
 ``W8A8ProjectionGroup`` runs them as one guarded linear over the
 concatenated output channels and returns one view per projection;
 ``quantize_qk(x, heads)`` turns such a Q or K view (sequence-major) into
-head-major INT8 codes with one scale per 128 tokens of each head.
+head-major INT8 codes with one scale per 128 tokens of each head;
+``rope_bf16(x, heads, cos, sin)`` applies the split-halves rotary embedding
+and ``rope_quantize_qk(x, heads, cos, sin)`` fuses it into that quantizer.
 """
 from __future__ import annotations
 
@@ -181,11 +183,7 @@ def rmsnorm_modulate_quantize_act(x: torch.Tensor, scale: torch.Tensor, shift: t
     return q, s
 
 
-def quantize_qk(x: torch.Tensor, heads: int, q=None, s=None):
-    """INT8 attention Q or K: ``x`` is bf16 [B, L, H*D] or [L, H*D],
-    sequence-major, with unit stride in the last dimension (a column slice
-    of a wider row is fine) -> (q int8 [B, H, L, D], s fp32 [B, H, ceil(L/128)]),
-    one scale per block of 128 tokens of each head (H = ``heads``)."""
+def _qk_view(x, heads):
     if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.bfloat16:
         raise ValueError("x must be a bf16 CUDA (HIP) tensor")
     x3 = x.unsqueeze(0) if x.dim() == 2 else x
@@ -197,6 +195,57 @@ def quantize_qk(x: torch.Tensor, heads: int, q=None, s=None):
     D, ld = HD // heads, x3.stride(1)
     if x3.stride(2) != 1 or (B > 1 and x3.stride(0) != L * ld):
         raise ValueError("rows of x must be evenly strided with unit-stride columns")
+    return x3, B, L, D, ld
+
+
+def _rope_tables(cos, sin, L, D):
+    for name, t in (("cos", cos), ("sin", sin)):
+        _need_cuda(name, t, torch.float32)
+        if tuple(t.shape) != (L, D // 2) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 [L, D/2] table")
+
+
+def rope_bf16(x: torch.Tensor, heads: int, cos: torch.Tensor, sin: torch.Tensor, out=None):
+    """Split-halves rotary embedding of Q or K: ``x`` bf16 [B, L, H*D] or
+    [L, H*D] as for ``quantize_qk``, ``cos``/``sin`` fp32 [L, D/2] -> bf16
+    of x's shape (contiguous)."""
+    x3, B, L, D, ld = _qk_view(x, heads)
+    _rope_tables(cos, sin, L, D)
+    if out is None:
+        out = torch.empty((B, L, heads * D), dtype=torch.bfloat16, device=x.device)
+    _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != B * L * heads * D or not out.is_contiguous():
+        raise ValueError("out must be contiguous with B*L*H*D elements")
+    check("w8a8_rope_bf16", lib().w8a8_rope_bf16(_ptr(x3), B, L, heads, D, ld, _ptr(cos), _ptr(sin), _ptr(out),
+                                                 _stream(x.device)))
+    return out.view(x.shape) if x.dim() == 2 else out.view(B, L, heads * D)
+
+
+def rope_quantize_qk(x: torch.Tensor, heads: int, cos: torch.Tensor, sin: torch.Tensor, q=None, s=None):
+    """``quantize_qk(rope_bf16(x, heads, cos, sin), heads)`` in one pass: the
+    rotated bf16 values are quantized without being written."""
+    x3, B, L, D, ld = _qk_view(x, heads)
+    _rope_tables(cos, sin, L, D)
+    nblk = -(-L // BLOCK)
+    if q is None:
+        q = torch.empty((B, heads, L, D), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = torch.empty((B, heads, nblk), dtype=torch.float32, device=x.device)
+    _need_cuda("q", q, torch.int8)
+    _need_cuda("s", s, torch.float32)
+    if q.numel() != B * heads * L * D or s.numel() != B * heads * nblk:
+        raise ValueError("output buffers have the wrong size")
+    check("w8a8_rope_quantize_qk", lib().w8a8_rope_quantize_qk(_ptr(x3), B, L, heads, D, ld, _ptr(cos), _ptr(sin),
+                                                               _ptr(q), _ptr(s), _stream(x.device)))
+    return (q, s) if x.dim() == 3 else (q[0], s[0])
+
+
+def quantize_qk(x: torch.Tensor, heads: int, q=None, s=None):
+    """INT8 attention Q or K: ``x`` is bf16 [B, L, H*D] or [L, H*D],
+    sequence-major, with unit stride in the last dimension (a column slice
+    of a wider row is fine) -> (q int8 [B, H, L, D], s fp32 [B, H, ceil(L/128)]),
+    one scale per block of 128 tokens of each head (H = ``heads``)."""
+    x3, B, L, D, ld = _qk_view(x, heads)
     nblk = -(-L // BLOCK)
     if q is None:
         q = torch.empty((B, heads, L, D), dtype=torch.int8, device=x.device)

@@ -24,7 +24,8 @@ EXPORTS = (
     "w8a8_debug_kblock_partials", "w8a8_status_string", "w8a8_last_hip_error",
     "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale_workspace_bytes",
     "w8a8_linear_postscale", "w8a8_gelu_bf16", "w8a8_gelu_quantize_act", "w8a8_quantize_qk",
-    "w8a8_rmsnorm_modulate_bf16", "w8a8_rmsnorm_modulate_quantize_act",
+    "w8a8_rmsnorm_modulate_bf16", "w8a8_rmsnorm_modulate_quantize_act", "w8a8_rope_bf16",
+    "w8a8_rope_quantize_qk",
 )
 POSTSCALE_MAX_K = 133120
 BLOCK_MAX_K = 4194304
@@ -70,6 +71,8 @@ def lib():
     L.w8a8_gelu_bf16.argtypes = [_P, _I64, _P, _P]
     L.w8a8_gelu_quantize_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
     L.w8a8_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
+    L.w8a8_rope_bf16.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]
+    L.w8a8_rope_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
     L.w8a8_rmsnorm_modulate_bf16.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P, _P]
     L.w8a8_rmsnorm_modulate_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P, _P,
                                                      _P]
@@ -79,7 +82,8 @@ def lib():
     for f in ("w8a8_quantize_weight", "w8a8_quantize_act", "w8a8_gemm_blockscale", "w8a8_linear",
               "w8a8_route", "w8a8_debug_kblock_partials", "w8a8_last_hip_error",
               "w8a8_quantize_rows", "w8a8_gemm_postscale", "w8a8_linear_postscale",
-              "w8a8_gelu_bf16", "w8a8_gelu_quantize_act", "w8a8_quantize_qk"):
+              "w8a8_gelu_bf16", "w8a8_gelu_quantize_act", "w8a8_quantize_qk", "w8a8_rope_bf16",
+              "w8a8_rope_quantize_qk", "w8a8_rmsnorm_modulate_bf16", "w8a8_rmsnorm_modulate_quantize_act"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

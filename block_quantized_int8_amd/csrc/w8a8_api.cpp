@@ -246,6 +246,44 @@ int w8a8_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_
     return hip_status(w8a8::launch_quantize_qk(static_cast<const uint16_t *>(x_bf16), B, L, H, D, ld, q, s, stream));
 }
 
+static int rope_args(const void *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
+                     const float *sin_t) {
+    if (!x || !cos_t || !sin_t || B <= 0 || L <= 0 || H <= 0 || D <= 0) return W8A8_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return W8A8_ERR_UNSUPPORTED;
+    if (H > INT32_MAX / D) return W8A8_ERR_UNSUPPORTED;
+    if (ld < H * D) return W8A8_ERR_INVALID_ARG;
+    if (ld % 8 || !aligned(x, 16) || !aligned(cos_t, 16) || !aligned(sin_t, 16)) return W8A8_ERR_UNSUPPORTED;
+    return W8A8_OK;
+}
+
+int w8a8_rope_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
+                   const float *sin_t, void *y_bf16, hipStream_t stream) {
+    if (!y_bf16) return W8A8_ERR_INVALID_ARG;
+    const int st = rope_args(x_bf16, B, L, H, D, ld, cos_t, sin_t);
+    if (st != W8A8_OK) return st;
+    if (B > INT64_MAX / L || B * L > INT64_MAX / (H * D)) return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(y_bf16, 16)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(cos_t) || !is_device_ptr(sin_t) || !is_device_ptr(y_bf16))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_rope_bf16(static_cast<const uint16_t *>(x_bf16), B, L, H, D, ld, cos_t, sin_t,
+                                             static_cast<uint16_t *>(y_bf16), stream));
+}
+
+int w8a8_rope_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                          const float *cos_t, const float *sin_t, int8_t *q, float *s, hipStream_t stream) {
+    if (!q || !s) return W8A8_ERR_INVALID_ARG;
+    const int st = rope_args(x_bf16, B, L, H, D, ld, cos_t, sin_t);
+    if (st != W8A8_OK) return st;
+    if (!aligned(q, 16) || !aligned(s, 4)) return W8A8_ERR_UNSUPPORTED;
+    const int64_t nblk = (L + W8A8_BLOCK - 1) / W8A8_BLOCK;
+    if (B > INT32_MAX / H || B * H > INT32_MAX / nblk) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(cos_t) || !is_device_ptr(sin_t) || !is_device_ptr(q) ||
+        !is_device_ptr(s))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_rope_quantize_qk(static_cast<const uint16_t *>(x_bf16), B, L, H, D, ld, cos_t,
+                                                    sin_t, q, s, stream));
+}
+
 int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
                                const void *shift_bf16, double eps, float *r_ws, void *y_bf16, hipStream_t stream) {
     const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, r_ws);

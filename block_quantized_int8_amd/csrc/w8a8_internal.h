@@ -36,6 +36,11 @@ hipError_t launch_gelu_quantize_block(const uint16_t *y, int64_t rows, int64_t c
 // Attention Q/K: sequence-major bf16 -> head-major int8 + per-128-token scales; D is 64 or 128.
 hipError_t launch_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
                               int8_t *q, float *s, hipStream_t stream);
+hipError_t launch_rope_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                                   const float *cos_t, const float *sin_t, int8_t *q, float *s,
+                                   hipStream_t stream);
+hipError_t launch_rope_bf16(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                            const float *cos_t, const float *sin_t, uint16_t *y, hipStream_t stream);
 
 // Modulated RMS normalization: r [rows] (fp32), y bf16, and y fused with the
 // 128x128 block quantization (rows and K multiples of 128, rows < 2^31).

@@ -287,6 +287,34 @@ int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L,
 int w8a8_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, int8_t *q,
                      float *s, hipStream_t stream);
 
+/*
+ * Split-halves rotary position embedding of attention Q or K (TurboT2VA
+ * paper, architecture-aware inference stack, fused-kernels paragraph, which
+ * lists split rotary embeddings among the fused patterns), which precedes
+ * their INT8 quantization:
+ *   input  x_bf16 as for w8a8_quantize_qk (element (b, l, h, d) at
+ *          x[(b*L + l)*ld + h*D + d]); cos_t and sin_t fp32 [L, D/2],
+ *          row-major, row l holding the angles of token position l for
+ *          pairs 0 .. D/2-1, shared by every batch entry and head;
+ *   rule   for d < D/2, with c = cos_t[l*D/2 + d], s = sin_t[l*D/2 + d]:
+ *            y(d)       = bf16(fl32(fl32(x(d) * c) - fl32(x(d + D/2) * s)))
+ *            y(d + D/2) = bf16(fl32(fl32(x(d + D/2) * c) + fl32(x(d) * s)))
+ *          each fl32 one IEEE fp32 operation (no fused multiply-add), bf16
+ *          to nearest even.
+ * w8a8_rope_bf16 writes y_bf16 [B*L, H*D] (sequence-major, contiguous).
+ * w8a8_rope_quantize_qk writes w8a8_quantize_qk's outputs (q [B, H, L, D],
+ * s [B, H, ceil(L/128)]) for the rotated values, which never reach memory;
+ * it equals, bit for bit, w8a8_quantize_qk applied to w8a8_rope_bf16's y.
+ * Requirements and errors as for w8a8_quantize_qk, plus: cos_t, sin_t (and
+ * y_bf16) 16-byte aligned device memory, else W8A8_ERR_UNSUPPORTED (host
+ * pointers: W8A8_ERR_INVALID_ARG).  x must not overlap y.  All buffers are
+ * the caller's; the calls are asynchronous on `stream`.
+ */
+int w8a8_rope_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
+                   const float *sin_t, void *y_bf16, hipStream_t stream);
+int w8a8_rope_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                          const float *cos_t, const float *sin_t, int8_t *q, float *s, hipStream_t stream);
+
 /* Static, human-readable name of a W8A8_* status code. */
 const char *w8a8_status_string(int status);
 

@@ -28,6 +28,10 @@ hipError_t launch_gelu_bf16(const uint16_t *, int64_t, uint16_t *, hipStream_t) 
 hipError_t launch_gelu_quantize_block(const uint16_t *, int64_t, int64_t, int8_t *, float *, hipStream_t) { reached("gelu_quantize"); }
 hipError_t launch_quantize_qk(const uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t, int8_t *, float *,
                               hipStream_t) { reached("quantize_qk"); }
+hipError_t launch_rope_quantize_qk(const uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t, const float *,
+                                   const float *, int8_t *, float *, hipStream_t) { reached("rope_quantize_qk"); }
+hipError_t launch_rope_bf16(const uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t, const float *, const float *,
+                            uint16_t *, hipStream_t) { reached("rope_bf16"); }
 hipError_t launch_gemm_bf16_tiled(const uint16_t *, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t,
                                   uint16_t *, hipStream_t) { reached("gemm_bf16_tiled"); }
 hipError_t launch_gemm_bf16(const void *, int, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t, uint16_t *,
@@ -105,6 +109,19 @@ int main() {
     CHECK(w8a8_quantize_qk(p, 1, 256, 2, 96, 192, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_quantize_qk(p, 1, 256, 2, 128, 255, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_quantize_qk(p, 1LL << 40, 256, 1LL << 20, 128, 1LL << 27, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    // rotary embedding: head dimension, stride, table alignment, sizes, missing outputs
+    CHECK(w8a8_rope_bf16(p, 1, 256, 2, 96, 192, f, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 255, f, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 260, f, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 256, f + 1, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 256, f, nullptr, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 256, f, f, nullptr, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rope_bf16(p, 1, 256, 1LL << 40, 128, 1LL << 47, f, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 256, f, f, p, nullptr) == W8A8_ERR_INVALID_ARG);  // host memory
+    CHECK(w8a8_rope_quantize_qk(p, 0, 256, 2, 128, 256, f, f, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rope_quantize_qk(p, 1, 256, 2, 64, 128, f, f, nullptr, f, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rope_quantize_qk(p, 1LL << 40, 256, 1LL << 20, 128, 1LL << 27, f, f, q8, f, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
     // modulated RMS normalization: eps, sizes, alignment, the fused path's block shape
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, 0.0, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, -1e-6, f, p, nullptr) == W8A8_ERR_INVALID_ARG);

@@ -134,3 +134,18 @@ def test_host_decided_errors_rmsnorm(L):
     assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 128, 192, fake, fake, 1e-6, fake, fake, fake, null) == 2
     assert L.w8a8_rmsnorm_modulate_quantize_act(ctypes.c_void_p(0x1008), 2, 128, 256, fake, fake, 1e-6, fake, fake,
                                                 fake, null) == 2
+
+
+def test_host_decided_errors_rope(L):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced
+    null = None
+    # head dimension 64 or 128, row stride >= H*D and a multiple of 8, 16-byte aligned tables
+    assert L.w8a8_rope_bf16(fake, 1, 256, 2, 96, 192, fake, fake, fake, null) == 2
+    assert L.w8a8_rope_bf16(fake, 1, 256, 2, 128, 255, fake, fake, fake, null) == 1
+    assert L.w8a8_rope_bf16(fake, 1, 256, 2, 128, 260, fake, fake, fake, null) == 2
+    assert L.w8a8_rope_bf16(fake, 1, 256, 2, 128, 256, ctypes.c_void_p(0x1004), fake, fake, null) == 2
+    assert L.w8a8_rope_bf16(fake, 1, 256, 2, 128, 256, fake, null, fake, null) == 1
+    assert L.w8a8_rope_quantize_qk(fake, 1, 0, 2, 128, 256, fake, fake, fake, fake, null) == 1
+    assert L.w8a8_rope_quantize_qk(fake, 1, 256, 2, 128, 256, fake, fake, null, fake, null) == 1
+    # host memory is refused before any launch
+    assert L.w8a8_rope_quantize_qk(fake, 1, 256, 2, 128, 256, fake, fake, fake, fake, null) == 1
