@@ -20,11 +20,13 @@ three; the MLP producer fused with the quantization (exact GELU + 128x128
 block quantize of the MLP's hidden activation, 32768 x 16384) against GELU
 and quantize run one after the other; the INT8 quantization of a video
 self-attention's Q and K (28672 tokens x 32 heads x 128, read from a fused
-Q/K/V output) into the head-major layout; the guard's bf16 fallback; and a
+Q/K/V output) into the head-major layout, and the same with the split-halves
+rotary embedding fused in front of it against rotation then quantization;
+the guard's bf16 fallback; and a
 two-stream step (an INT8 linear and a guarded-to-bf16 linear launched on
 two streams at once).
 
-Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk
+Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|rope|rms
 launches just that work for --steps iterations (no oracle);
 --copy-calibration runs a plain 1 GiB device copy used to scale the HBM byte
 counters.
@@ -68,6 +70,11 @@ RMS_BYTES = RB * RL * RK * 3 + (RB * RL // 128) * (RK // 128) * 4 + 2 * RB * RK 
 # attention Q or K of one video self-attention: read bf16, write int8 + one scale per 128 tokens x head
 AL, AH, AD = 28672, 32, 128
 QK_BYTES = AL * AH * AD * 3 + AH * (AL // 128) * 4
+# the same with the rotary embedding in front: plus the fp32 cos and sin
+# tables [AL, AD/2] (latent grid 16 frames x 56 x 32 for the three axes)
+ROPE_GRID = (16, 56, 32)
+ROPE_TABLE_BYTES = AL * (AD // 2) * 4 * 2
+ROPE_QK_BYTES = QK_BYTES + ROPE_TABLE_BYTES
 
 
 def log(msg):
@@ -193,6 +200,13 @@ def qk_buffers(dev):
     return qkv, qq, sq
 
 
+def rope_tables_dev(dev):
+    import torch
+    from block_quantized_int8_amd.workloads import rope_tables
+    cs, sn = rope_tables(AL, AD, grid=ROPE_GRID)
+    return torch.from_numpy(cs).to(dev), torch.from_numpy(sn).to(dev)
+
+
 def rms_buffers(dev):
     """A transformer block's hidden state (B = 4 x L = 8192 tokens x 4096)
     with its modulation, and the producer's outputs."""
@@ -229,7 +243,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "rms"],
+    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "rope", "rms"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -281,6 +295,15 @@ def main():
             w8a8.quantize_qk(qkv[:, :AH * AD], AH, qq, sq)
         torch.cuda.synchronize()
         log(f"--only qk: {args.steps} launches done")
+        return
+
+    if args.only == "rope":
+        qkv, qq, sq = qk_buffers(dev)
+        cs, sn = rope_tables_dev(dev)
+        for _ in range(args.steps):
+            w8a8.rope_quantize_qk(qkv[:, :AH * AD], AH, cs, sn, qq, sq)
+        torch.cuda.synchronize()
+        log(f"--only rope: {args.steps} launches done")
         return
 
     if args.only == "rms":
@@ -400,9 +423,33 @@ def main():
             qk_t.append((a, b))
     torch.cuda.synchronize()
     qk_us = sum(a.elapsed_time(b) for a, b in qk_t) / len(qk_t) * 1e3
-    del qkv, qq, sq
     log(f"Q/K INT8 [{AL}, {AH}x{AD}] from a fused QKV output: {qk_us:.1f} us per tensor "
         f"({QK_BYTES / qk_us / 1e3:.0f} GB/s)")
+
+    # rotary embedding + Q/K INT8: fused vs rotation to bf16 then quantization
+    cs, sn = rope_tables_dev(dev)
+    yrot = torch.empty((AL, AH * AD), dtype=torch.bfloat16, device=dev)
+    w8a8.rope_quantize_qk(qkv[:, :AH * AD], AH, cs, sn, qq, sq)   # untimed first launches
+    w8a8.rope_bf16(qkv[:, :AH * AD], AH, cs, sn, out=yrot)
+    torch.cuda.synchronize()
+    rope_runs = {"fused": lambda v: w8a8.rope_quantize_qk(v, AH, cs, sn, qq, sq),
+                 "rotate": lambda v: w8a8.rope_bf16(v, AH, cs, sn, out=yrot),
+                 "quantize": lambda v: w8a8.quantize_qk(yrot, AH, qq, sq)}
+    rope_t = {k: [] for k in rope_runs}
+    for i in range(args.steps):
+        for col in (0, AH * AD):
+            for k, fn in rope_runs.items():
+                flush.amax()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn(qkv[:, col:col + AH * AD])
+                b.record()
+                rope_t[k].append((a, b))
+    torch.cuda.synchronize()
+    rope_us = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in rope_t.items()}
+    del qkv, qq, sq, yrot, cs, sn
+    log(f"RoPE + Q/K INT8 fused {rope_us['fused']:.1f} us per tensor vs rotate {rope_us['rotate']:.1f} + "
+        f"quantize {rope_us['quantize']:.1f} us")
 
     # the guard's bf16 fallback on the shapes that take it: M = 4000 (not a
     # multiple of 128) at 4096^2, and the two-stream workload's 1000 x 2048^2
@@ -613,6 +660,18 @@ def main():
                         "us": round(qk_us, 2), "gbs": round(QK_BYTES / qk_us / 1e3, 1),
                         "frac_of_hbm": round(QK_BYTES / qk_us / 1e3 / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": QK_BYTES},
+        "rope_qk_ab": {"note": "split-halves rotary embedding fused into the INT8 Q/K quantizer vs rotation "
+                               "to bf16 then quantization, per Q or K tensor of the video self-attention "
+                               "(not part of a step); tables fp32 [tokens, head_dim/2]",
+                       "shape": {"tokens": AL, "heads": AH, "head_dim": AD, "row_stride": 3 * AH * AD,
+                                 "table_grid": list(ROPE_GRID)},
+                       "fused_us": round(rope_us["fused"], 2),
+                       "fused_gbs_algorithmic": round(ROPE_QK_BYTES / rope_us["fused"] / 1e3, 1),
+                       "fused_frac_of_hbm": round(ROPE_QK_BYTES / rope_us["fused"] / 1e3 / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes": ROPE_QK_BYTES,
+                       "unfused_rotate_us": round(rope_us["rotate"], 2),
+                       "unfused_quantize_us": round(rope_us["quantize"], 2),
+                       "speedup": round((rope_us["rotate"] + rope_us["quantize"]) / rope_us["fused"], 3)},
         "rmsnorm_producer_ab": {"note": "transformer-block input: modulated RMSNorm fused with the 128x128 "
                                         "block quantize vs the normalization then the quantizer (not part of a "
                                         "step); the fused entry reads x twice (row norms, then the blocks)",

@@ -274,7 +274,7 @@ int w8a8_rope_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, i
     if (!q || !s) return W8A8_ERR_INVALID_ARG;
     const int st = rope_args(x_bf16, B, L, H, D, ld, cos_t, sin_t);
     if (st != W8A8_OK) return st;
-    if (!aligned(q, 16) || !aligned(s, 4)) return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(s, 4) || ld > W8A8_ROPE_MAX_LD) return W8A8_ERR_UNSUPPORTED;
     const int64_t nblk = (L + W8A8_BLOCK - 1) / W8A8_BLOCK;
     if (B > INT32_MAX / H || B * H > INT32_MAX / nblk) return W8A8_ERR_UNSUPPORTED;
     if (!is_device_ptr(x_bf16) || !is_device_ptr(cos_t) || !is_device_ptr(sin_t) || !is_device_ptr(q) ||

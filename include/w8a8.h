@@ -63,6 +63,9 @@ enum { W8A8_PATH_INT8 = 0, W8A8_PATH_BF16 = 1 };
 /* Largest K of the block-scale GEMM: it addresses a 256-row operand tile
  * with 32-bit byte offsets (256 * K < 2^31). */
 #define W8A8_BLOCK_MAX_K 4194304
+/* Largest row stride (in elements) of the rotary embedding's fused Q/K entry,
+ * whose per-block buffer offsets are 32-bit. */
+#define W8A8_ROPE_MAX_LD 4194304
 
 /*
  * Static weight quantization (done once, at load): w_bf16 [N, K] ->
@@ -307,7 +310,8 @@ int w8a8_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_
  * it equals, bit for bit, w8a8_quantize_qk applied to w8a8_rope_bf16's y.
  * Requirements and errors as for w8a8_quantize_qk, plus: cos_t, sin_t (and
  * y_bf16) 16-byte aligned device memory, else W8A8_ERR_UNSUPPORTED (host
- * pointers: W8A8_ERR_INVALID_ARG).  x must not overlap y.  All buffers are
+ * pointers: W8A8_ERR_INVALID_ARG); w8a8_rope_quantize_qk also needs
+ * ld <= W8A8_ROPE_MAX_LD (else W8A8_ERR_UNSUPPORTED).  x must not overlap y.  All buffers are
  * the caller's; the calls are asynchronous on `stream`.
  */
 int w8a8_rope_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
