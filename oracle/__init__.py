@@ -50,10 +50,12 @@ def lib():
         L.oracle_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
         L.oracle_rmsnorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
         L.oracle_rope.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
+        L.oracle_gated_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
         for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
                   "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
                   "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
-                  "oracle_quantize_qk", "oracle_rmsnorm_modulate", "oracle_rope"):
+                  "oracle_quantize_qk", "oracle_rmsnorm_modulate", "oracle_rope",
+                  "oracle_gated_residual"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -244,3 +246,16 @@ def rope_quantize_qk(x_bf16, B, L, H, D, ld, cos_t, sin_t):
     """The fused Q/K producer's result: the rotary embedding rounded to bf16,
     then quantize_qk of that (contiguous) result -> (q [B, H, L, D], s)."""
     return quantize_qk(rope(x_bf16, B, L, H, D, ld, cos_t, sin_t), B, L, H, D, H * D)
+
+
+def gated_residual(h_bf16: np.ndarray, o_bf16: np.ndarray, gate_bf16: np.ndarray, L: int):
+    """y = bf16(h + gate[i // L] * o) for rows i of h and o [B*L, N]; gate [B, N]."""
+    h = _c(h_bf16, np.uint16)
+    o = _c(o_bf16, np.uint16)
+    g = _c(gate_bf16, np.uint16)
+    R, N = h.shape
+    if o.shape != (R, N) or R % L or g.shape != (R // L, N):
+        raise ValueError("shapes: h, o [B*L, N], gate [B, N]")
+    y = np.empty((R, N), np.uint16)
+    _check(lib().oracle_gated_residual(_ptr(h), _ptr(o), _ptr(g), R // L, L, N, _ptr(y)), "gated_residual")
+    return y

@@ -26,6 +26,8 @@
  *   - INT8 query/key of the sparse attention, block rule over 128 tokens x
  *       head dim, rearranged sequence-major -> head-major: TurboT2VA paper,
  *       same section, sparse-attention paragraph.
+ *   - gated residual update h + g * o of a linear's output: same section,
+ *       fused-kernels paragraph (gated residual updates).
  *   - rotary position embedding in the split-halves form on Q and K ahead
  *       of their INT8 quantization: same section, fused-kernels paragraph
  *       (split rotary embeddings among the fused patterns).
@@ -364,6 +366,33 @@ int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64
                 }
                 q[(bh * L + l) * D + d] = out;
             }
+    }
+    return OR_OK;
+}
+
+/*
+ * Gated residual update of a transformer block (TurboT2VA paper,
+ * architecture-aware inference stack, fused-kernels paragraph: gated residual
+ * updates among the fused patterns), applied to a linear's bf16 output o and
+ * the residual stream h, both [B*L, N], with a gate per batch entry and
+ * channel g [B, N]:
+ *   y[i, n] = bf16( fl32( h[i, n] + fl32( g[i / L, n] * o[i, n] ) ) )
+ * each fl32 one IEEE fp32 operation (the product of two bf16 is exact in
+ * fp32), bf16 to nearest even.  The sum's fp32 rounding can land on a bf16
+ * tie that the exact sum would miss, so this is not always the exact value
+ * rounded once.  y may alias h or o exactly.
+ */
+int oracle_gated_residual(const uint16_t *h, const uint16_t *o, const uint16_t *gate, int64_t B, int64_t L,
+                          int64_t N, uint16_t *y) {
+    if (!h || !o || !gate || !y || B <= 0 || L <= 0 || N <= 0) return OR_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < B * L; ++i) {
+        const int64_t b = i / L;
+        for (int64_t n = 0; n < N; ++n) {
+            const float p = oracle_bf16_to_f32(gate[b * N + n]) * oracle_bf16_to_f32(o[i * N + n]);
+            const float s = oracle_bf16_to_f32(h[i * N + n]) + p;
+            y[i * N + n] = oracle_f64_to_bf16((double)s);
+        }
     }
     return OR_OK;
 }

@@ -21,8 +21,8 @@ the definitions:
   scales and bias once at the end);
 * INT8 attention Q/K (TurboT2VA paper, sparse-attention paragraph): the
   block rule over 128 tokens x the head dimension, per batch and head;
-* the modulated RMS normalization and the split-halves rotary embedding
-  (TurboT2VA paper, fused-kernels paragraph).
+* the modulated RMS normalization, the split-halves rotary embedding and
+  the gated residual update (TurboT2VA paper, fused-kernels paragraph).
 
 Everything is O(M*N*K) Python-level numpy on small arrays: use it on
 inputs of a few hundred rows at most.
@@ -230,4 +230,21 @@ def rope(x_bits: np.ndarray, B: int, L: int, H: int, D: int, ld: int, cos_t: np.
             hi = (x2 * c).astype(np.float32) + (x1 * s).astype(np.float32)
             y[row, h * D:h * D + half] = f64_to_bf16_array(lo.astype(np.float32).astype(np.float64))
             y[row, h * D + half:h * D + D] = f64_to_bf16_array(hi.astype(np.float32).astype(np.float64))
+    return y
+
+
+# ------------------------------------------------------- gated residual update
+
+def gated_residual(h_bits: np.ndarray, o_bits: np.ndarray, gate_bits: np.ndarray, L: int) -> np.ndarray:
+    """Row i: bf16(fl32(h + fl32(gate[i // L] * o))), each fl32 one numpy fp32
+    operation, then one rounding to bf16."""
+    h = bf16_to_f64(h_bits).astype(np.float32)
+    o = bf16_to_f64(o_bits).astype(np.float32)
+    g = bf16_to_f64(gate_bits).astype(np.float32)
+    R, N = h.shape
+    y = np.zeros((R, N), np.uint16)
+    for i in range(R):
+        p = (g[i // L] * o[i]).astype(np.float32)
+        s = (h[i] + p).astype(np.float32)
+        y[i] = f64_to_bf16_array(s.astype(np.float64))
     return y

@@ -24,6 +24,8 @@ int oracle_linear_postscale_rows(const int8_t *qx, const float *sx, const int8_t
 int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, int8_t *q,
                        float *s);
 int oracle_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight);
+int oracle_gated_residual(const uint16_t *h, const uint16_t *o, const uint16_t *gate, int64_t B, int64_t L,
+                          int64_t N, uint16_t *y);
 int oracle_rope(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
                 const float *sin_t, uint16_t *y);
 int oracle_rmsnorm_modulate(const uint16_t *x, int64_t B, int64_t L, int64_t K, const uint16_t *scale,
@@ -105,6 +107,14 @@ int main(void) {
     CHECK(oracle_rope(qkx, B, L, H, D, ld, rc, rs, ry) == 0);
     CHECK(oracle_rope(qkx, B, L, H, D - 1, ld, rc, rs, ry) != 0);      /* odd head dimension */
     CHECK(oracle_rope(qkx, B, L, H, D, H * D - 1, rc, rs, ry) != 0);
+
+    /* gated residual update, out of place and in place */
+    uint16_t *gh = bf16_buf(4 * 3 * 40), *go = bf16_buf(4 * 3 * 40), *gg = bf16_buf(4 * 40),
+             *gy = xmalloc(sizeof(uint16_t) * 4 * 3 * 40);
+    CHECK(oracle_gated_residual(gh, go, gg, 4, 3, 40, gy) == 0);
+    CHECK(oracle_gated_residual(gh, go, gg, 4, 3, 40, gh) == 0);
+    CHECK(oracle_gated_residual(gh, go, gg, 4, 0, 40, gy) != 0);
+    free(gh); free(go); free(gg); free(gy);
 
     /* modulated RMS normalization, with its r */
     uint16_t *nsc = bf16_buf(2 * K), *nsh = bf16_buf(2 * K), *ny = xmalloc(sizeof(uint16_t) * M * K);
