@@ -26,7 +26,7 @@ the guard's bf16 fallback; and a
 two-stream step (an INT8 linear and a guarded-to-bf16 linear launched on
 two streams at once).
 
-Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|rope|rms
+Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|rope|rms|residual
 launches just that work for --steps iterations (no oracle);
 --copy-calibration runs a plain 1 GiB device copy used to scale the HBM byte
 counters.
@@ -67,6 +67,11 @@ GELU_BYTES = HM * HK * 2 * 2                                              # read
 # write int8 + block scales, read the [B, K] scale and shift
 RB, RL, RK = 4, 8192, 4096
 RMS_BYTES = RB * RL * RK * 3 + (RB * RL // 128) * (RK // 128) * 4 + 2 * RB * RK * 2
+# gated residual update of the attention projection's output: 4 batch
+# entries; the fused GEMM reads h and writes y instead of writing o, the
+# update kernel reads h and o and writes y
+RES_B = 4
+RES_UPDATE_BYTES = M * N * 2 * 3 + RES_B * N * 2
 # attention Q or K of one video self-attention: read bf16, write int8 + one scale per 128 tokens x head
 AL, AH, AD = 28672, 32, 128
 QK_BYTES = AL * AH * AD * 3 + AH * (AL // 128) * 4
@@ -200,6 +205,18 @@ def qk_buffers(dev):
     return qkv, qq, sq
 
 
+def residual_buffers(dev):
+    """Residual stream h [M, N] and gate [4, N] (4 batch entries of M/4
+    tokens) for the attention projection's gated residual update, and its
+    output."""
+    import numpy as np
+    import torch
+    from block_quantized_int8_amd.workloads import random_bf16
+    h = torch.from_numpy(random_bf16(93, (M, N), 2.0).view(np.int16)).to(dev).view(torch.bfloat16)
+    g = torch.from_numpy(random_bf16(94, (RES_B, N), 0.5).view(np.int16)).to(dev).view(torch.bfloat16)
+    return h, g, torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+
 def rope_tables_dev(dev):
     import torch
     from block_quantized_int8_amd.workloads import rope_tables
@@ -243,7 +260,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "rope", "rms"],
+    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "rope", "rms",
+                                       "residual"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -304,6 +322,15 @@ def main():
             w8a8.rope_quantize_qk(qkv[:, :AH * AD], AH, cs, sn, qq, sq)
         torch.cuda.synchronize()
         log(f"--only rope: {args.steps} launches done")
+        return
+
+    if args.only == "residual":
+        hres, gres, yres = residual_buffers(dev)
+        w8a8.quantize_act(x, qx, sx)
+        for _ in range(args.steps):
+            w8a8.gemm_blockscale_gated_residual(qx, sx, qw, sw, hres, gres, out=yres)
+        torch.cuda.synchronize()
+        log(f"--only residual: {args.steps} launches done")
         return
 
     if args.only == "rms":
@@ -407,6 +434,31 @@ def main():
     qkv_sep_us = sa.elapsed_time(sb) / args.steps * 1e3
     del group, projs, wk, wv
     log(f"QKV 32768x(3x4096)x4096: one group {qkv_group_us:.1f} us vs three linears {qkv_sep_us:.1f} us")
+
+    # gated residual update h + gate * o of the attention projection's output
+    # (4 batch entries x 8192 tokens): in the GEMM's epilogue vs the GEMM then
+    # the update kernel; each launch after a read flush
+    hres, gres, yres = residual_buffers(dev)
+    res_runs = {"fused": lambda: w8a8.gemm_blockscale_gated_residual(qx, sx, qw, sw, hres, gres, out=yres),
+                "gemm": lambda: w8a8.gemm_blockscale(qx, sx, qw, sw, out=y),
+                "update": lambda: w8a8.gated_residual(hres, y, gres, out=yres)}
+    for fn in res_runs.values():
+        fn()
+    torch.cuda.synchronize()
+    res_t = {k: [] for k in res_runs}
+    for i in range(args.steps):
+        for k, fn in res_runs.items():
+            flush.amax()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            res_t[k].append((a, b))
+    torch.cuda.synchronize()
+    res_us = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in res_t.items()}
+    del hres, gres, yres
+    log(f"gated residual: fused GEMM {res_us['fused']:.1f} us vs GEMM {res_us['gemm']:.1f} + update "
+        f"{res_us['update']:.1f} us")
 
     # INT8 attention Q and K from the fused Q/K/V output (row stride 3 * 4096)
     qkv, qq, sq = qk_buffers(dev)
@@ -660,6 +712,16 @@ def main():
                         "us": round(qk_us, 2), "gbs": round(QK_BYTES / qk_us / 1e3, 1),
                         "frac_of_hbm": round(QK_BYTES / qk_us / 1e3 / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": QK_BYTES},
+        "gated_residual_ab": {"note": "gated residual update h + gate * o of the attention projection's output "
+                                      "(4 batch entries of 8192 tokens) in the block GEMM's epilogue vs the GEMM "
+                                      "then the update kernel (not part of a step)",
+                              "shape": [M, N, K], "batch_entries": RES_B,
+                              "fused_us": round(res_us["fused"], 2),
+                              "fused_tops": round(GEMM_OPS / (res_us["fused"] * 1e-6) / 1e12, 1),
+                              "unfused_gemm_us": round(res_us["gemm"], 2),
+                              "unfused_update_us": round(res_us["update"], 2),
+                              "update_gbs": round(RES_UPDATE_BYTES / res_us["update"] / 1e3, 1),
+                              "speedup": round((res_us["gemm"] + res_us["update"]) / res_us["fused"], 3)},
         "rope_qk_ab": {"note": "split-halves rotary embedding fused into the INT8 Q/K quantizer vs rotation "
                                "to bf16 then quantization, per Q or K tensor of the video self-attention "
                                "(not part of a step); tables fp32 [tokens, head_dim/2]",

@@ -29,6 +29,10 @@ concatenated output channels and returns one view per projection;
 head-major INT8 codes with one scale per 128 tokens of each head;
 ``rope_bf16(x, heads, cos, sin)`` applies the split-halves rotary embedding
 and ``rope_quantize_qk(x, heads, cos, sin)`` fuses it into that quantizer.
+
+Consumer fused with the GEMM: ``gated_residual(h, o, gate)`` (h + gate * o),
+``gemm_blockscale_gated_residual`` (the update in the block GEMM's epilogue)
+and ``W8A8Linear.forward_gated_residual(x, h, gate)``.
 """
 from __future__ import annotations
 
@@ -260,6 +264,48 @@ def quantize_qk(x: torch.Tensor, heads: int, q=None, s=None):
     return (q, s) if x.dim() == 3 else (q[0], s[0])
 
 
+def _residual_args(h, gate, M, N):
+    _need_cuda("h", h, torch.bfloat16)
+    _need_cuda("gate", gate, torch.bfloat16)
+    if h.numel() != M * N or not h.is_contiguous():
+        raise ValueError("h must be contiguous with the output's M x N elements")
+    if gate.dim() != 2 or gate.shape[1] != N or not gate.is_contiguous() or M % gate.shape[0]:
+        raise ValueError("gate must be a contiguous [B, N] tensor with B dividing the rows")
+    return M // gate.shape[0]
+
+
+def gated_residual(h: torch.Tensor, o: torch.Tensor, gate: torch.Tensor, out=None):
+    """Gated residual update y = bf16(h + gate[b] * o): h and o bf16
+    [..., N] with B*L rows, gate bf16 [B, N] (row i takes gate row i // L).
+    ``out`` may be ``h`` or ``o`` (in place)."""
+    _need_cuda("o", o, torch.bfloat16)
+    N = o.shape[-1]
+    M = o.numel() // N
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    L = _residual_args(h, gate, M, N)
+    if out is None:
+        out = torch.empty_like(o)
+    _need_cuda("out", out, torch.bfloat16)
+    check("w8a8_gated_residual", lib().w8a8_gated_residual(_ptr(h), _ptr(o), _ptr(gate), M // L, L, N, _ptr(out),
+                                                           _stream(o.device)))
+    return out
+
+
+def gemm_blockscale_gated_residual(qx, sx, qw, sw, h, gate, bias=None, out=None):
+    """``gated_residual(h, gemm_blockscale(qx, sx, qw, sw, bias), gate)`` with
+    the update in the GEMM's epilogue; ``out`` may be ``h`` (in place)."""
+    M, K = qx.shape
+    N = qw.shape[0]
+    L = _residual_args(h, gate, M, N)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
+    check("w8a8_gemm_blockscale_gated_residual",
+          lib().w8a8_gemm_blockscale_gated_residual(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(bias), M, N, K,
+                                                    _ptr(h), _ptr(gate), L, _ptr(out), _stream(qx.device)))
+    return out
+
+
 def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):
     """INT8 GEMM with per-K-block dequantization -> bf16 [M, N]."""
     _need_cuda("qx", qx, torch.int8)
@@ -479,6 +525,40 @@ class W8A8Linear(torch.nn.Module):
         out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
         self.last_path = PATH_INT8
         return out.view(*x.shape[:-1], N)
+
+
+    def forward_gated_residual(self, x: torch.Tensor, h: torch.Tensor, gate: torch.Tensor,
+                               out=None) -> torch.Tensor:
+        """``gated_residual(h, self(x), gate)``: h bf16 with the output's shape,
+        gate bf16 [B, N]; on the INT8 block path the update runs in the GEMM's
+        epilogue, so the layer's output never reaches memory.  ``out`` must
+        not overlap h."""
+        if self.scaling != "block":
+            return gated_residual(h, self.forward(x), gate, out)
+        N, K = self.weight.shape
+        x2 = x.reshape(-1, K)
+        if not x2.is_contiguous():
+            x2 = x2.contiguous()
+        if x2.dtype not in _DTYPES:
+            raise ValueError("x must be a bf16, fp16 or fp32 tensor")
+        _need_cuda("x", x2)
+        M = x2.shape[0]
+        L = _residual_args(h, gate, M, N)
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        _need_cuda("out", out, torch.bfloat16)
+        need = workspace_bytes(M, K) if self.qweight is not None else 0
+        if need and (self._workspace is None or self._workspace.numel() < need
+                     or self._workspace.device != x.device):
+            self._workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        path = ctypes.c_int(-1)
+        check("w8a8_linear_gated_residual",
+              lib().w8a8_linear_gated_residual(_ptr(x2), _DTYPES[x2.dtype], M, K, N, _ptr(self.weight),
+                                               _ptr(self.qweight), _ptr(self.wscale), _ptr(self.bias), _ptr(h),
+                                               _ptr(gate), L, _ptr(out), _ptr(self._workspace) if need else None,
+                                               need, _stream(x.device), ctypes.byref(path)))
+        self.last_path = path.value
+        return out.reshape(*x.shape[:-1], N)
 
 
 class W8A8ProjectionGroup(torch.nn.Module):

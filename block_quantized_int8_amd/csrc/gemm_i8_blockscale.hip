@@ -131,16 +131,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const int8_t *base, 
 }
 
 // kMode: kBlockScaled (the block form), kPartials (test epilogue),
-// kPostScaled (per-row / per-channel scales applied once at the end) or
+// kPostScaled (per-row / per-channel scales applied once at the end),
 // kBf16 (bf16 operands, fp32 accumulation: the fallback's fast path; the
-// sizes in Problem then count bytes along K).
-enum { kBlockScaled = 0, kPartialsOnly = 1, kPostScaled = 2, kBf16 = 3 };
+// sizes in Problem then count bytes along K) or kBlockResidual (the block
+// form whose bf16 output o feeds a gated residual update in the epilogue:
+// y = bf16(fl32(h + fl32(gate[row / L] * o))), read from Residual).
+enum { kBlockScaled = 0, kPartialsOnly = 1, kPostScaled = 2, kBf16 = 3, kBlockResidual = 4 };
+
+// Operands of the gated residual epilogue: residual stream h [M, N] (may be
+// y itself), gate [M / L, N], L rows per gate row.
+struct Residual {
+    const uint16_t *h;
+    const uint16_t *gate;
+    int64_t L;
+};
 
 template <int kMode>
 __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     const int8_t *__restrict__ qx, const float *__restrict__ sx, const int8_t *__restrict__ qw,
     const float *__restrict__ sw, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
-    int32_t *__restrict__ partials, const Problem p) {
+    int32_t *__restrict__ partials, const Problem p, const Residual res) {
+    constexpr bool kBlockForm = kMode == kBlockScaled || kMode == kBlockResidual;
     constexpr bool kPartials = kMode == kPartialsOnly;
     constexpr bool kPost = kMode == kPostScaled;
     constexpr bool kBf = kMode == kBf16;
@@ -193,8 +204,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     const bool active = (m_org + wm * kWaveM < p.m_end) && (n_org + wn * kWaveN < p.n_end);
     const int64_t mblk = (m_org + wm * kWaveM) / kBlock;
     const int64_t nblk = (n_org + wn * kWaveN) / kBlock;
-    const float *sxr = kMode == kBlockScaled ? sx + mblk * KB : nullptr;
-    const float *swr = kMode == kBlockScaled ? sw + nblk * KB : nullptr;
+    const float *sxr = kBlockForm ? sx + mblk * KB : nullptr;
+    const float *swr = kBlockForm ? sw + nblk * KB : nullptr;
     // combined scales sx*sw of 64 consecutive K-blocks, one per lane; each
     // K-block reads its own with readlane (no scalar load, whose lgkmcnt
     // wait would also drain every LDS read in flight)
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
     // partial edge tile may not exist)
     float sc_lane = 0.0f;
     auto load_scales = [&](int kb0) {
-        if constexpr (kMode == kBlockScaled) {
+        if constexpr (kBlockForm) {
             const int kb = kb0 + lane;
             sc_lane = (active && kb < KB) ? sxr[kb] * swr[kb] : 0.0f;
         }
@@ -257,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
             for (int kk = 0; kk < 4; ++kk)
                 fx[1][kk] = *reinterpret_cast<const i32x4 *>(xs + 32 * kBlock + fofs[kk]);
             float scale = 0.0f;
-            if constexpr (kMode == kBlockScaled)
+            if constexpr (kBlockForm)
                 scale = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lane), kb & 63));
 
             // software pipeline: the MFMAs of sub-tile s run while the VALU
@@ -384,19 +395,54 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_bs_kernel(
         const int c = lane & 15;
         uint16_t *yrow = y + (m_org + wm * kWaveM) * p.N + n_org + wn * kWaveN + c * 8;
         const int64_t rows_left = p.m_end - (m_org + wm * kWaveM);  // < 64 only in a ragged last tile
+        if constexpr (kMode == kBlockResidual) {
+            // gated residual: every row's h and gate chunk is requested
+            // before the first is used; the same lane reads h and writes y at
+            // one address, so y may be h itself
+            const int64_t off = (m_org + wm * kWaveM) * p.N + n_org + wn * kWaveN + c * 8;
+            const uint32_t grow0 = (uint32_t)(m_org + wm * kWaveM), L = (uint32_t)res.L;
+            const uint16_t *gcol = res.gate + n_org + wn * kWaveN + c * 8;
+            i32x4 hv[kWaveM / 4], gv[kWaveM / 4];
 #pragma unroll
-        for (int it = 0; it < kWaveM / 4; ++it) {
-            const int row = it * 4 + (lane >> 4);
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(ot + row * 256 + ((c ^ (row & 15)) << 4));
-            if (row < rows_left)
-                __builtin_nontemporal_store(v, reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N));
+            for (int it = 0; it < kWaveM / 4; ++it) {
+                const int row = it * 4 + (lane >> 4);
+                const bool in = row < rows_left;
+                hv[it] = in ? __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(res.h + off + (int64_t)row * p.N))
+                            : i32x4{0, 0, 0, 0};
+                gv[it] = in ? *reinterpret_cast<const i32x4 *>(gcol + (int64_t)((grow0 + row) / L) * p.N)
+                            : i32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int it = 0; it < kWaveM / 4; ++it) {
+                const int row = it * 4 + (lane >> 4);
+                const i32x4 v = *reinterpret_cast<const i32x4 *>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+                i32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t ow = (uint32_t)v[e], hw = (uint32_t)hv[it][e], gw = (uint32_t)gv[it][e];
+                    const float y0 = bf16_to_f32(hw & 0xFFFFu) + bf16_to_f32(gw & 0xFFFFu) * bf16_to_f32(ow & 0xFFFFu);
+                    const float y1 = bf16_to_f32(hw >> 16) + bf16_to_f32(gw >> 16) * bf16_to_f32(ow >> 16);
+                    out[e] = (int)pack_bf16x2(y0, y1);
+                }
+                if (row < rows_left)
+                    __builtin_nontemporal_store(out, reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N));
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < kWaveM / 4; ++it) {
+                const int row = it * 4 + (lane >> 4);
+                const i32x4 v = *reinterpret_cast<const i32x4 *>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+                if (row < rows_left)
+                    __builtin_nontemporal_store(v, reinterpret_cast<i32x4 *>(yrow + (int64_t)row * p.N));
+            }
         }
     }
 }
 
 template <int kMode>
 hipError_t launch(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
-                  const uint16_t *bias, uint16_t *y, int32_t *partials, Problem p, hipStream_t stream) {
+                  const uint16_t *bias, uint16_t *y, int32_t *partials, Problem p, hipStream_t stream,
+                  Residual res = Residual{nullptr, nullptr, 1}) {
     const int64_t tm = (p.m_end - p.m_begin + kTileM - 1) / kTileM;
     const int64_t tn = (p.n_end - p.n_begin + kTileN - 1) / kTileN;
     if (tm <= 0 || tn <= 0 || p.K < kBlock) return hipSuccess;
@@ -404,7 +450,7 @@ hipError_t launch(const int8_t *qx, const float *sx, const int8_t *qw, const flo
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
     gemm_i8_bs_kernel<kMode><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
-        qx, sx, qw, sw, bias, y, partials, p);
+        qx, sx, qw, sw, bias, y, partials, p, res);
     return hipGetLastError();
 }
 
@@ -415,6 +461,15 @@ hipError_t launch_gemm_i8_blockscale(const int8_t *qx, const float *sx, const in
                                      int64_t K, uint16_t *y, hipStream_t stream) {
     Problem p{N, K, 0, M, 0, N, 0, 0};
     return launch<kBlockScaled>(qx, sx, qw, sw, bias, y, nullptr, p, stream);
+}
+
+hipError_t launch_gemm_i8_blockscale_residual(const int8_t *qx, const float *sx, const int8_t *qw,
+                                              const float *sw, const uint16_t *bias, int64_t M, int64_t N,
+                                              int64_t K, const uint16_t *h, const uint16_t *gate, int64_t L,
+                                              uint16_t *y, hipStream_t stream) {
+    if (L <= 0 || M > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit row arithmetic in the epilogue
+    Problem p{N, K, 0, M, 0, N, 0, 0};
+    return launch<kBlockResidual>(qx, sx, qw, sw, bias, y, nullptr, p, stream, Residual{h, gate, L});
 }
 
 hipError_t launch_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N,

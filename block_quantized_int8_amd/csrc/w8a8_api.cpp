@@ -142,6 +142,102 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, con
                                              static_cast<uint16_t *>(y_bf16), stream));
 }
 
+// Two equally sized ranges that overlap without coinciding (exact aliasing
+// is the in-place case some entries allow).
+static bool partial_overlap(const void *a, const void *b, size_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x != y && (x < y ? y - x : x - y) < bytes;
+}
+
+static int residual_args(const void *h, const void *gate, int64_t M, int64_t N, int64_t L, const void *y) {
+    if (!h || !gate || L <= 0 || M % L) return W8A8_ERR_INVALID_ARG;
+    if (partial_overlap(y, h, (size_t)M * (size_t)N * 2)) return W8A8_ERR_INVALID_ARG;
+    if (N % 8 || !aligned(h, 16) || !aligned(gate, 16) || !aligned(y, 16)) return W8A8_ERR_UNSUPPORTED;
+    return W8A8_OK;
+}
+
+int w8a8_gated_residual(const void *h_bf16, const void *o_bf16, const void *gate_bf16, int64_t B, int64_t L,
+                        int64_t N, void *y_bf16, hipStream_t stream) {
+    if (!o_bf16 || !y_bf16 || B <= 0 || L <= 0 || N <= 0) return W8A8_ERR_INVALID_ARG;
+    if (B > INT64_MAX / L || B * L > INT64_MAX / N / 2) return W8A8_ERR_UNSUPPORTED;
+    const int st = residual_args(h_bf16, gate_bf16, B * L, N, L, y_bf16);
+    if (st != W8A8_OK) return st;
+    if (partial_overlap(y_bf16, o_bf16, (size_t)(B * L) * (size_t)N * 2)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(o_bf16, 16)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(h_bf16) || !is_device_ptr(o_bf16) || !is_device_ptr(gate_bf16) || !is_device_ptr(y_bf16))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_gated_residual(static_cast<const uint16_t *>(h_bf16),
+                                                  static_cast<const uint16_t *>(o_bf16),
+                                                  static_cast<const uint16_t *>(gate_bf16), B, L, N,
+                                                  static_cast<uint16_t *>(y_bf16), stream));
+}
+
+int w8a8_gemm_blockscale_gated_residual(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                                        const void *bias_bf16, int64_t M, int64_t N, int64_t K,
+                                        const void *h_bf16, const void *gate_bf16, int64_t L, void *y_bf16,
+                                        hipStream_t stream) {
+    if (!qx || !sx || !qw || !sw || !y_bf16 || M <= 0 || N <= 0 || K <= 0) return W8A8_ERR_INVALID_ARG;
+    const int st = residual_args(h_bf16, gate_bf16, M, N, L, y_bf16);
+    if (st != W8A8_OK) return st;
+    if (!mult128(M) || !mult128(N) || !mult128(K) || K > W8A8_BLOCK_MAX_K || M > INT32_MAX)
+        return W8A8_ERR_UNSUPPORTED;
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(sx, 4) || !aligned(sw, 4) || !aligned(bias_bf16, 8))
+        return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(qx) || !is_device_ptr(sx) || !is_device_ptr(qw) || !is_device_ptr(sw) ||
+        !is_device_ptr(y_bf16) || !is_device_ptr(h_bf16) || !is_device_ptr(gate_bf16) ||
+        (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_gemm_i8_blockscale_residual(
+        qx, sx, qw, sw, static_cast<const uint16_t *>(bias_bf16), M, N, K, static_cast<const uint16_t *>(h_bf16),
+        static_cast<const uint16_t *>(gate_bf16), L, static_cast<uint16_t *>(y_bf16), stream));
+}
+
+int w8a8_linear_gated_residual(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
+                               const int8_t *qw, const float *sw, const void *bias_bf16, const void *h_bf16,
+                               const void *gate_bf16, int64_t L, void *y_bf16, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream, int *path_out) {
+    if (!x || !w_bf16 || !y_bf16 || M <= 0 || K <= 0 || N <= 0 || !valid_dtype(x_dtype))
+        return W8A8_ERR_INVALID_ARG;
+    if ((qw == nullptr) != (sw == nullptr)) return W8A8_ERR_INVALID_ARG;
+    const int st = residual_args(h_bf16, gate_bf16, M, N, L, y_bf16);
+    if (st != W8A8_OK) return st;
+    if (h_bf16 == y_bf16) return W8A8_ERR_INVALID_ARG;  // the fallback writes o into y before the update
+    if (!is_device_ptr(x) || !is_device_ptr(w_bf16) || !is_device_ptr(y_bf16) || !is_device_ptr(h_bf16) ||
+        !is_device_ptr(gate_bf16) || (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+
+    int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
+    if (path == W8A8_PATH_INT8 && (K > W8A8_BLOCK_MAX_K || M > INT32_MAX)) path = W8A8_PATH_BF16;
+    if (path == W8A8_PATH_INT8) {
+        const size_t need = w8a8_linear_workspace_bytes(M, K);
+        if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
+        if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace)) return W8A8_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || !aligned(qw, 16) || !aligned(workspace, 16) || !aligned(sw, 4) ||
+            !aligned(bias_bf16, 8))
+            path = W8A8_PATH_BF16;
+    }
+    if (path_out) *path_out = path;
+
+    if (path == W8A8_PATH_INT8) {
+        int8_t *qx = static_cast<int8_t *>(workspace);
+        float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) + round256((size_t)M * (size_t)K));
+        hipError_t e = w8a8::launch_quantize_block(static_cast<const uint16_t *>(x), M, K, qx, sx, stream);
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(w8a8::launch_gemm_i8_blockscale_residual(
+            qx, sx, qw, sw, static_cast<const uint16_t *>(bias_bf16), M, N, K,
+            static_cast<const uint16_t *>(h_bf16), static_cast<const uint16_t *>(gate_bf16), L,
+            static_cast<uint16_t *>(y_bf16), stream));
+    }
+    hipError_t e = w8a8::launch_gemm_bf16(x, x_dtype, static_cast<const uint16_t *>(w_bf16),
+                                          static_cast<const uint16_t *>(bias_bf16), M, N, K,
+                                          static_cast<uint16_t *>(y_bf16), stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(w8a8::launch_gated_residual(static_cast<const uint16_t *>(h_bf16),
+                                                  static_cast<const uint16_t *>(y_bf16),
+                                                  static_cast<const uint16_t *>(gate_bf16), M / L, L, N,
+                                                  static_cast<uint16_t *>(y_bf16), stream));
+}
+
 int w8a8_debug_kblock_partials(const int8_t *qx, const int8_t *qw, int64_t M, int64_t N, int64_t K,
                                int64_t m0, int64_t mt, int64_t n0, int64_t nt, int32_t *partials,
                                hipStream_t stream) {

@@ -34,6 +34,12 @@ hipError_t launch_gelu_quantize_block(const uint16_t *y, int64_t rows, int64_t c
                                       hipStream_t stream);
 
 // Attention Q/K: sequence-major bf16 -> head-major int8 + per-128-token scales; D is 64 or 128.
+hipError_t launch_gemm_i8_blockscale_residual(const int8_t *qx, const float *sx, const int8_t *qw,
+                                              const float *sw, const uint16_t *bias, int64_t M, int64_t N,
+                                              int64_t K, const uint16_t *h, const uint16_t *gate, int64_t L,
+                                              uint16_t *y, hipStream_t stream);
+hipError_t launch_gated_residual(const uint16_t *h, const uint16_t *o, const uint16_t *gate, int64_t B, int64_t L,
+                                 int64_t N, uint16_t *y, hipStream_t stream);
 hipError_t launch_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
                               int8_t *q, float *s, hipStream_t stream);
 hipError_t launch_rope_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,

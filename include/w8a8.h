@@ -264,6 +264,49 @@ int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L,
                                        hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Gated residual update (TurboT2VA paper, architecture-aware inference stack,
+ * fused-kernels paragraph, which lists gated residual updates among the fused
+ * patterns): the residual stream h takes a linear's output o scaled by a
+ * gate per batch entry and channel,
+ *   y[i, n] = bf16( fl32( h[i, n] + fl32( gate[i / L, n] * o[i, n] ) ) )
+ * each fl32 one IEEE fp32 operation, bf16 to nearest even.  h, o, y are bf16
+ * [B*L, N] = [M, N] row-major; gate bf16 [B, N]; L = rows (tokens) per batch
+ * entry.  N must be a multiple of 8 and h, o, gate, y 16-byte aligned (else
+ * W8A8_ERR_UNSUPPORTED); null pointers, sizes <= 0, M not a multiple of L, or
+ * a y that overlaps h (or o) without coinciding -> W8A8_ERR_INVALID_ARG.
+ * All buffers are the caller's device memory; calls are asynchronous on
+ * `stream`.  Inputs must be finite (a sum may round to +-Inf).
+ * ------------------------------------------------------------------------- */
+
+/* The update alone: y may be h or o itself (in place). */
+int w8a8_gated_residual(const void *h_bf16, const void *o_bf16, const void *gate_bf16, int64_t B, int64_t L,
+                        int64_t N, void *y_bf16, hipStream_t stream);
+
+/*
+ * w8a8_gemm_blockscale whose bf16 output o (bias included) feeds the update
+ * in the GEMM's epilogue: o is rounded to bf16 exactly as w8a8_gemm_blockscale
+ * writes it and never reaches memory, so the result equals, bit for bit,
+ * w8a8_gated_residual applied to w8a8_gemm_blockscale's output.  Requirements
+ * of both, plus M <= INT32_MAX; y may be h itself (in place).
+ */
+int w8a8_gemm_blockscale_gated_residual(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                                        const void *bias_bf16, int64_t M, int64_t N, int64_t K,
+                                        const void *h_bf16, const void *gate_bf16, int64_t L, void *y_bf16,
+                                        hipStream_t stream);
+
+/*
+ * The guarded layer followed by the update: w8a8_linear's routing, workspace
+ * and errors; on the INT8 path quantize + the fused GEMM above, on the bf16
+ * fallback the bf16 GEMM into y and then the update in place on y.  y must
+ * not overlap h (W8A8_ERR_INVALID_ARG), since the fallback writes o into y
+ * first; N a multiple of 8 and h, gate, y 16-byte aligned on both paths.
+ */
+int w8a8_linear_gated_residual(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
+                               const int8_t *qw, const float *sw, const void *bias_bf16, const void *h_bf16,
+                               const void *gate_bf16, int64_t L, void *y_bf16, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream, int *path_out);
+
+/* ---------------------------------------------------------------------------
  * INT8 query/key for the sparse attention (TurboT2VA paper, architecture-
  * aware inference stack, sparse-attention paragraph: query and key are
  * quantized to INT8, and the sequence-major tensors are rearranged into the

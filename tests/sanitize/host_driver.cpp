@@ -32,6 +32,11 @@ hipError_t launch_rope_quantize_qk(const uint16_t *, int64_t, int64_t, int64_t, 
                                    const float *, int8_t *, float *, hipStream_t) { reached("rope_quantize_qk"); }
 hipError_t launch_rope_bf16(const uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t, const float *, const float *,
                             uint16_t *, hipStream_t) { reached("rope_bf16"); }
+hipError_t launch_gemm_i8_blockscale_residual(const int8_t *, const float *, const int8_t *, const float *,
+                                              const uint16_t *, int64_t, int64_t, int64_t, const uint16_t *,
+                                              const uint16_t *, int64_t, uint16_t *, hipStream_t) { reached("gemm_residual"); }
+hipError_t launch_gated_residual(const uint16_t *, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t,
+                                 uint16_t *, hipStream_t) { reached("gated_residual"); }
 hipError_t launch_gemm_bf16_tiled(const uint16_t *, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t,
                                   uint16_t *, hipStream_t) { reached("gemm_bf16_tiled"); }
 hipError_t launch_gemm_bf16(const void *, int, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t, uint16_t *,
@@ -120,8 +125,27 @@ int main() {
     CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 256, f, f, p, nullptr) == W8A8_ERR_INVALID_ARG);  // host memory
     CHECK(w8a8_rope_quantize_qk(p, 0, 256, 2, 128, 256, f, f, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_rope_quantize_qk(p, 1, 256, 2, 64, 128, f, f, nullptr, f, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rope_quantize_qk(p, 1, 256, 2, 128, W8A8_ROPE_MAX_LD + 8, f, f, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_rope_quantize_qk(p, 1LL << 40, 256, 1LL << 20, 128, 1LL << 27, f, f, q8, f, nullptr) ==
           W8A8_ERR_UNSUPPORTED);
+    // gated residual: L dividing the rows, N a multiple of 8, partial overlap, aliasing
+    char *pc = static_cast<char *>(p);
+    CHECK(w8a8_gated_residual(p, p, p, 2, 64, 256, p, nullptr) == W8A8_ERR_INVALID_ARG);        // host memory
+    CHECK(w8a8_gated_residual(p, p, p, 2, 0, 256, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_gated_residual(p, p, p, 2, 64, 252, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gated_residual(p, p, p, 2, 64, 256, pc + 16, nullptr) == W8A8_ERR_INVALID_ARG);  // overlaps h
+    CHECK(w8a8_gated_residual(p, pc + (1 << 20), pc + 8, 2, 64, 256, pc + (2 << 20), nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gemm_blockscale_gated_residual(q8, f, q8, f, nullptr, 256, 256, 256, p, p, 3, p, nullptr) ==
+          W8A8_ERR_INVALID_ARG);                                                                  // 3 does not divide M
+    CHECK(w8a8_gemm_blockscale_gated_residual(q8, f, q8, f, nullptr, 256, 256, 200, p, p, 128, pc + (1 << 20),
+                                              nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_gemm_blockscale_gated_residual(q8, f, q8, f, nullptr, 256, 256, 256, nullptr, p, 128, p, nullptr) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear_gated_residual(p, 0, 256, 256, 256, p, q8, f, nullptr, p, p, 128, p, p, 1 << 20, nullptr,
+                                     &path) == W8A8_ERR_INVALID_ARG);                             // y == h
+    CHECK(w8a8_linear_gated_residual(p, 0, 256, 256, 256, p, q8, f, nullptr, p, p, 128, pc + (1 << 20), p, 1 << 20,
+                                     nullptr, &path) == W8A8_ERR_INVALID_ARG);                    // host memory
+    CHECK(path == -7);
     // modulated RMS normalization: eps, sizes, alignment, the fused path's block shape
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, 0.0, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, -1e-6, f, p, nullptr) == W8A8_ERR_INVALID_ARG);

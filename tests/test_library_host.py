@@ -147,5 +147,26 @@ def test_host_decided_errors_rope(L):
     assert L.w8a8_rope_bf16(fake, 1, 256, 2, 128, 256, fake, null, fake, null) == 1
     assert L.w8a8_rope_quantize_qk(fake, 1, 0, 2, 128, 256, fake, fake, fake, fake, null) == 1
     assert L.w8a8_rope_quantize_qk(fake, 1, 256, 2, 128, 256, fake, fake, null, fake, null) == 1
+    # the fused entry's row stride limit (32-bit buffer offsets)
+    big = 4194304 + 8
+    assert L.w8a8_rope_quantize_qk(fake, 1, 256, 2, 128, big, fake, fake, fake, fake, null) == 2
     # host memory is refused before any launch
     assert L.w8a8_rope_quantize_qk(fake, 1, 256, 2, 128, 256, fake, fake, fake, fake, null) == 1
+
+
+def test_host_decided_errors_gated_residual(L):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced
+    far = ctypes.c_void_p(0x4000000)
+    null = None
+    assert L.w8a8_gated_residual(fake, fake, fake, 2, 64, 252, far, null) == 2           # N % 8
+    assert L.w8a8_gated_residual(fake, fake, fake, 2, 0, 256, far, null) == 1
+    assert L.w8a8_gated_residual(fake, fake, fake, 2, 64, 256, ctypes.c_void_p(0x100010), null) == 1  # overlaps h
+    assert L.w8a8_gated_residual(fake, fake, fake, 2, 64, 256, far, null) == 1           # host memory
+    assert L.w8a8_gemm_blockscale_gated_residual(fake, fake, fake, fake, null, 256, 256, 256, fake, fake, 3, far,
+                                                 null) == 1                              # L must divide M
+    assert L.w8a8_gemm_blockscale_gated_residual(fake, fake, fake, fake, null, 256, 256, 200, fake, fake, 128, far,
+                                                 null) == 2
+    path = ctypes.c_int(-7)
+    assert L.w8a8_linear_gated_residual(fake, 0, 256, 256, 256, fake, fake, fake, null, fake, fake, 128, fake,
+                                        fake, 1 << 20, null, ctypes.byref(path)) == 1   # y == h
+    assert path.value == -7
