@@ -93,3 +93,60 @@ def test_producer_and_qk_replay():
         assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
         kq_o, ks_o = oracle.quantize_qk(host, 1, M, H, D, K)
         assert np.array_equal(kq.cpu().numpy(), kq_o[0]) and np.array_equal(ks.cpu().numpy(), ks_o[0])
+
+
+def test_block_slice_replay():
+    # a transformer-block slice in one graph: modulated RMSNorm fused into the
+    # projection input's quantization, the block GEMM with the gated residual
+    # update in its epilogue (in place on the residual stream h), then the
+    # rotary embedding fused into the INT8 quantization of the updated stream
+    # read as 2 heads of 128 (standing in for a Q projection)
+    B, L, K, H, D = 2, 256, 256, 2, 128
+    M = B * L
+    w = to_dev_bf16(random_bf16(60, (K, K), 0.02))
+    layer = w8a8.W8A8Linear(w)
+    x = torch.empty((B, L, K), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    sc = to_dev_bf16(random_bf16(61, (B, K), 0.3))
+    sh = to_dev_bf16(random_bf16(62, (B, K), 0.3))
+    gate = to_dev_bf16(random_bf16(63, (B, K), 0.5))
+    from block_quantized_int8_amd.workloads import rope_tables
+    cs_h, sn_h = rope_tables(L, D)
+    cs, sn = torch.from_numpy(cs_h).cuda(), torch.from_numpy(sn_h).cuda()
+    qx = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sx = torch.empty((M // 128, K // 128), dtype=torch.float32, device="cuda")
+    kq = torch.empty((B, H, L, D), dtype=torch.int8, device="cuda")
+    ks = torch.empty((B, H, L // 128), dtype=torch.float32, device="cuda")
+
+    def work():
+        w8a8.rmsnorm_modulate_quantize_act(x, sc, sh, 1e-6, qx, sx)
+        w8a8.gemm_blockscale_gated_residual(qx, sx, layer.qweight, layer.wscale, h, gate, out=h)
+        w8a8.rope_quantize_qk(h.view(B, L, K), H, cs, sn, kq, ks)
+
+    def load(seed):
+        xh, hh = random_bf16(seed, (M, K), 2.0), random_bf16(seed + 1, (M, K), 2.0)
+        x.copy_(to_dev_bf16(xh).view(B, L, K))
+        h.copy_(to_dev_bf16(hh))
+        return xh, hh
+
+    load(64)
+    g = capture(work)
+    for seed in (66, 68):
+        xh, hh = load(seed)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (qx.clone(), sx.clone(), h.clone(), kq.clone(), ks.clone())
+        load(seed)
+        work()                                  # eager, same inputs
+        torch.cuda.synchronize()
+        for a, b in zip(got, (qx, sx, h, kq, ks)):
+            assert torch.equal(a.view(torch.int8), b.view(torch.int8)), f"replay with input seed {seed}"
+    # the last replay against the oracle: codes bit-exact, the updated stream
+    # within the output tolerance, and its rotation + Q/K codes bit-exact
+    oq, os_ = oracle.rmsnorm_modulate_quantize_block(xh, L, bf16_bits(sc), bf16_bits(sh), 1e-6)
+    assert np.array_equal(got[0].cpu().numpy(), oq) and np.array_equal(got[1].cpu().numpy(), os_)
+    wq, ws = oracle.quantize_block(bf16_bits(w))
+    want_h = oracle.gated_residual(hh, oracle.linear_int8(oq, os_, wq, ws), bf16_bits(gate), L)
+    assert_bf16_close(bf16_bits(got[2]), want_h, "graph replay: GEMM + gated residual")
+    rq, rs = oracle.rope_quantize_qk(bf16_bits(got[2]), B, L, H, D, K, cs_h, sn_h)
+    assert np.array_equal(got[3].cpu().numpy(), rq) and np.array_equal(got[4].cpu().numpy(), rs)
