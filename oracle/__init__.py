@@ -51,11 +51,12 @@ def lib():
         L.oracle_rmsnorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
         L.oracle_rope.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
         L.oracle_gated_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
+        L.oracle_layernorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
         for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
                   "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
                   "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
                   "oracle_quantize_qk", "oracle_rmsnorm_modulate", "oracle_rope",
-                  "oracle_gated_residual"):
+                  "oracle_gated_residual", "oracle_layernorm_modulate"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -226,6 +227,32 @@ def rmsnorm_modulate_quantize_block(x_bf16, L, scale_bf16, shift_bf16, eps=1e-6)
     """The fused producer's result: the modulated RMS normalization rounded to
     bf16, then the 128x128 block quantization of that matrix -> (q, s)."""
     return quantize_block(rmsnorm_modulate(x_bf16, L, scale_bf16, shift_bf16, eps))
+
+
+def layernorm_modulate(x_bf16: np.ndarray, L: int, scale_bf16: np.ndarray, shift_bf16: np.ndarray,
+                       eps: float = 1e-6, want_stats: bool = False):
+    """Modulated layer normalization of x [B*L, K] (bf16 bits) with per-batch
+    scale and shift [B, K] -> y bf16 bits [B*L, K] (and fp32 (mean, r) [B*L, 2])."""
+    x = _c(x_bf16, np.uint16)
+    sc = _c(scale_bf16, np.uint16)
+    sh = _c(shift_bf16, np.uint16)
+    R, K = x.shape
+    if R % L:
+        raise ValueError("rows must be a multiple of L")
+    B = R // L
+    if sc.shape != (B, K) or sh.shape != (B, K):
+        raise ValueError("scale and shift must be [B, K]")
+    y = np.empty((R, K), np.uint16)
+    st = np.empty((R, 2), np.float32)
+    _check(lib().oracle_layernorm_modulate(_ptr(x), B, L, K, _ptr(sc), _ptr(sh), float(eps), _ptr(y), _ptr(st)),
+           "layernorm_modulate")
+    return (y, st) if want_stats else y
+
+
+def layernorm_modulate_quantize_block(x_bf16, L, scale_bf16, shift_bf16, eps=1e-6):
+    """The fused producer's result: the modulated layer normalization rounded
+    to bf16, then the 128x128 block quantization of that matrix -> (q, s)."""
+    return quantize_block(layernorm_modulate(x_bf16, L, scale_bf16, shift_bf16, eps))
 
 
 def rope(x_bf16: np.ndarray, B: int, L: int, H: int, D: int, ld: int, cos_t: np.ndarray, sin_t: np.ndarray):

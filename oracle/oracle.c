@@ -26,6 +26,8 @@
  *   - INT8 query/key of the sparse attention, block rule over 128 tokens x
  *       head dim, rearranged sequence-major -> head-major: TurboT2VA paper,
  *       same section, sparse-attention paragraph.
+ *   - modulated layer normalization (mean and variance, no affine weight):
+ *       same section, fused-kernels paragraph (LayerNorm replaced).
  *   - gated residual update h + g * o of a linear's output: same section,
  *       fused-kernels paragraph (gated residual updates).
  *   - rotary position embedding in the split-halves form on Q and K ahead
@@ -366,6 +368,50 @@ int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64
                 }
                 q[(bh * L + l) * D + d] = out;
             }
+    }
+    return OR_OK;
+}
+
+/*
+ * Modulated layer normalization (TurboT2VA paper, architecture-aware
+ * inference stack, fused-kernels paragraph: module-level LayerNorm replaced,
+ * adaptive scale-shift modulation fused), without an affine weight.  For row
+ * i = b*L + l of x [B*L, K]:
+ *   mu  = sum_k x_ik / K,   var = sum_k (x_ik - mu)^2 / K    (fp64, two passes)
+ *   m_i = fl32(mu),   r_i = fl32( 1 / sqrt(var + eps) )
+ *   y_ik = bf16( fl32( fl32( fl32( fl32(x_ik - m_i) * r_i ) * fl32(1 + scale[b,k]) ) + shift[b,k] ) )
+ * each fl32 one IEEE fp32 operation, bf16 to nearest even.  stats_out, if
+ * given, receives (m_i, r_i) as two floats per row.
+ */
+int oracle_layernorm_modulate(const uint16_t *x, int64_t B, int64_t L, int64_t K, const uint16_t *scale,
+                              const uint16_t *shift, double eps, uint16_t *y, float *stats_out) {
+    if (!x || !scale || !shift || !y || B <= 0 || L <= 0 || K <= 0 || !(eps > 0.0)) return OR_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < B * L; ++i) {
+        const int64_t b = i / L;
+        const uint16_t *xr = x + i * K;
+        double S = 0.0;
+        for (int64_t k = 0; k < K; ++k) S += (double)oracle_bf16_to_f32(xr[k]);
+        const double mu = S / (double)K;
+        double V = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double d = (double)oracle_bf16_to_f32(xr[k]) - mu;
+            V += d * d;
+        }
+        const float m = (float)mu;
+        const float r = (float)(1.0 / sqrt(V / (double)K + eps));
+        if (stats_out) {
+            stats_out[2 * i] = m;
+            stats_out[2 * i + 1] = r;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            const float c = oracle_bf16_to_f32(xr[k]) - m;
+            const float t = c * r;
+            const float one_s = 1.0f + oracle_bf16_to_f32(scale[b * K + k]);
+            const float u = t * one_s;
+            const float v = u + oracle_bf16_to_f32(shift[b * K + k]);
+            y[i * K + k] = oracle_f64_to_bf16((double)v);
+        }
     }
     return OR_OK;
 }

@@ -21,8 +21,9 @@ the definitions:
   scales and bias once at the end);
 * INT8 attention Q/K (TurboT2VA paper, sparse-attention paragraph): the
   block rule over 128 tokens x the head dimension, per batch and head;
-* the modulated RMS normalization, the split-halves rotary embedding and
-  the gated residual update (TurboT2VA paper, fused-kernels paragraph).
+* the modulated RMS and layer normalizations, the split-halves rotary
+  embedding and the gated residual update (TurboT2VA paper, fused-kernels
+  paragraph).
 
 Everything is O(M*N*K) Python-level numpy on small arrays: use it on
 inputs of a few hundred rows at most.
@@ -205,6 +206,32 @@ def rmsnorm_modulate(x_bits: np.ndarray, L: int, scale_bits: np.ndarray, shift_b
         r = np.float32(1.0 / math.sqrt(S / K + eps))
         for k in range(K):
             t = np.float32(np.float32(x[i, k]) * r)
+            u = np.float32(t * np.float32(np.float32(1.0) + sc[b, k]))
+            v = np.float32(u + sh[b, k])
+            y[i, k] = f64_to_bf16_bits(float(v))
+    return y
+
+
+def layernorm_modulate(x_bits: np.ndarray, L: int, scale_bits: np.ndarray, shift_bits: np.ndarray,
+                       eps: float = 1e-6) -> np.ndarray:
+    """Row i = b*L + l: the mean (exact sum, math.fsum) and the variance of
+    the deviations from it in fp64, m = fl32(mean), r = fl32(1 / sqrt(var +
+    eps)); then per element, each step one fp32 rounding:
+    bf16((((x - m) * r) * (1 + scale[b])) + shift[b])."""
+    x = bf16_to_f64(x_bits)
+    sc = bf16_to_f64(scale_bits).astype(np.float32)
+    sh = bf16_to_f64(shift_bits).astype(np.float32)
+    R, K = x.shape
+    y = np.zeros((R, K), np.uint16)
+    for i in range(R):
+        b = i // L
+        mu = math.fsum(float(v) for v in x[i]) / K
+        var = math.fsum((float(v) - mu) ** 2 for v in x[i]) / K
+        m = np.float32(mu)
+        r = np.float32(1.0 / math.sqrt(var + eps))
+        for k in range(K):
+            c = np.float32(np.float32(x[i, k]) - m)
+            t = np.float32(c * r)
             u = np.float32(t * np.float32(np.float32(1.0) + sc[b, k]))
             v = np.float32(u + sh[b, k])
             y[i, k] = f64_to_bf16_bits(float(v))

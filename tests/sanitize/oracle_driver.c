@@ -24,6 +24,8 @@ int oracle_linear_postscale_rows(const int8_t *qx, const float *sx, const int8_t
 int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, int8_t *q,
                        float *s);
 int oracle_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight);
+int oracle_layernorm_modulate(const uint16_t *x, int64_t B, int64_t L, int64_t K, const uint16_t *scale,
+                              const uint16_t *shift, double eps, uint16_t *y, float *stats_out);
 int oracle_gated_residual(const uint16_t *h, const uint16_t *o, const uint16_t *gate, int64_t B, int64_t L,
                           int64_t N, uint16_t *y);
 int oracle_rope(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
@@ -121,6 +123,12 @@ int main(void) {
     float *nr = xmalloc(sizeof(float) * M);
     CHECK(oracle_rmsnorm_modulate(x, 2, M / 2, K, nsc, nsh, 1e-6, ny, nr) == 0);
     CHECK(oracle_rmsnorm_modulate(x, 2, M / 2, K, nsc, nsh, 1e-6, ny, NULL) == 0);
+    /* modulated layer normalization, with and without its statistics */
+    float *nst = xmalloc(sizeof(float) * 2 * M);
+    CHECK(oracle_layernorm_modulate(x, 2, M / 2, K, nsc, nsh, 1e-6, ny, nst) == 0);
+    CHECK(oracle_layernorm_modulate(x, 2, M / 2, K, nsc, nsh, 1e-6, ny, NULL) == 0);
+    CHECK(oracle_layernorm_modulate(x, 2, M / 2, K, nsc, nsh, 0.0, ny, NULL) != 0);
+    free(nst);
 
     /* GELU over every bf16 pattern (NaN/Inf included: defined output, no UB) */
     uint16_t *gin = xmalloc(sizeof(uint16_t) * 65536), *gout = xmalloc(sizeof(uint16_t) * 65536);
