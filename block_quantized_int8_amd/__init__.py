@@ -20,7 +20,9 @@ Post-scale form (per-row / per-output-channel scales, scales applied once):
 
 Producer fused with the quantization: ``gelu_bf16(x)`` (exact GELU, bf16 in
 and out), ``gelu_quantize_act(y)`` (block quantization of bf16(GELU(y))
-without writing it) and ``W8A8Linear.forward_gelu(y)`` = layer(GELU(y)).
+without writing it) and ``W8A8Linear.forward_gelu(y)`` = layer(GELU(y));
+likewise ``rmsnorm_modulate_*`` / ``layernorm_modulate_*`` and
+``W8A8Linear.forward_modulated(x, scale, shift, norm=...)``.
 
 Projections sharing one input (Q/K/V, or cross-attention K/V):
 ``W8A8ProjectionGroup`` runs them as one guarded linear over the
@@ -184,6 +186,46 @@ def rmsnorm_modulate_quantize_act(x: torch.Tensor, scale: torch.Tensor, shift: t
     check("w8a8_rmsnorm_modulate_quantize_act",
           lib().w8a8_rmsnorm_modulate_quantize_act(_ptr(x3), B, L, K, _ptr(scale), _ptr(shift), float(eps),
                                                    _ptr(r), _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def layernorm_modulate_bf16(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6,
+                            out=None):
+    """Modulated layer normalization of bf16 x [B, L, K] with per-batch scale
+    and shift [B, K]: bf16((x - mean) * r * (1 + scale) + shift),
+    r = 1/sqrt(var + eps), no affine weight."""
+    x3, B, L, K = _modulation_args(x, scale, shift)
+    if out is None:
+        out = torch.empty_like(x)
+    _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != x3.numel() or not out.is_contiguous():
+        raise ValueError("out must be contiguous with as many elements as x")
+    st = torch.empty(2 * B * L, dtype=torch.float32, device=x.device)  # the entry point's workspace
+    check("w8a8_layernorm_modulate_bf16",
+          lib().w8a8_layernorm_modulate_bf16(_ptr(x3), B, L, K, _ptr(scale), _ptr(shift), float(eps), _ptr(st),
+                                             _ptr(out), _stream(x.device)))
+    return out
+
+
+def layernorm_modulate_quantize_act(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6,
+                                    q=None, s=None):
+    """Block quantization of the modulated layer normalization of x
+    [B, L, K], fused (the bf16 result is never written) -> (q int8 [B*L, K],
+    s fp32 [B*L/128, K/128])."""
+    x3, B, L, K = _modulation_args(x, scale, shift)
+    M = B * L
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = torch.empty((max(M // BLOCK, 1), max(K // BLOCK, 1)), dtype=torch.float32, device=x.device)
+    _need_cuda("q", q, torch.int8)
+    _need_cuda("s", s, torch.float32)
+    if q.numel() != M * K or s.numel() < (M // BLOCK) * (K // BLOCK):
+        raise ValueError("output buffers have the wrong size")
+    st = torch.empty(2 * M, dtype=torch.float32, device=x.device)     # the entry point's workspace
+    check("w8a8_layernorm_modulate_quantize_act",
+          lib().w8a8_layernorm_modulate_quantize_act(_ptr(x3), B, L, K, _ptr(scale), _ptr(shift), float(eps),
+                                                     _ptr(st), _ptr(q), _ptr(s), _stream(x.device)))
     return q, s
 
 
@@ -500,11 +542,16 @@ class W8A8Linear(torch.nn.Module):
 
 
     def forward_modulated(self, x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
-                          eps: float = 1e-6) -> torch.Tensor:
+                          eps: float = 1e-6, norm: str = "rms") -> torch.Tensor:
         """``self(rmsnorm_modulate_bf16(x, scale, shift, eps))`` for bf16 x
-        [B, L, K]: the modulated normalization fused into the input
-        quantization when the INT8 block path applies; otherwise it runs
-        alone and ``forward`` takes its own guarded path."""
+        [B, L, K] (``norm="layer"``: ``layernorm_modulate_bf16``): the
+        modulated normalization fused into the input quantization when the
+        INT8 block path applies; otherwise it runs alone and ``forward``
+        takes its own guarded path."""
+        if norm not in ("rms", "layer"):
+            raise ValueError("norm must be 'rms' or 'layer'")
+        alone, fused_fn = ((rmsnorm_modulate_bf16, rmsnorm_modulate_quantize_act) if norm == "rms"
+                           else (layernorm_modulate_bf16, layernorm_modulate_quantize_act))
         N, K = self.weight.shape
         x3, B, L, Kx = _modulation_args(x, scale, shift)
         if Kx != K:
@@ -514,14 +561,14 @@ class W8A8Linear(torch.nn.Module):
                  and route(torch.bfloat16, M, K, N, True) == PATH_INT8 and x3.data_ptr() % 16 == 0
                  and scale.data_ptr() % 16 == 0 and shift.data_ptr() % 16 == 0)
         if not fused:
-            return self.forward(rmsnorm_modulate_bf16(x, scale, shift, eps))
+            return self.forward(alone(x, scale, shift, eps))
         need = workspace_bytes(M, K)
         if self._workspace is None or self._workspace.numel() < need or self._workspace.device != x.device:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
         s_off = (M * K + 255) // 256 * 256
         q = self._workspace[:M * K].view(torch.int8).view(M, K)
         s = self._workspace[s_off:s_off + 4 * (M // BLOCK) * (K // BLOCK)].view(torch.float32)
-        rmsnorm_modulate_quantize_act(x3, scale, shift, eps, q, s.view(M // BLOCK, K // BLOCK))
+        fused_fn(x3, scale, shift, eps, q, s.view(M // BLOCK, K // BLOCK))
         out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
         self.last_path = PATH_INT8
         return out.view(*x.shape[:-1], N)

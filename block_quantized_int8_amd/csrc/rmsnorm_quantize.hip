@@ -1,5 +1,5 @@
-// Modulated RMS normalization, alone and fused with the 128x128 block INT8
-// quantization of its result, for gfx950.
+// Modulated RMS and layer normalization, alone and fused with the 128x128
+// block INT8 quantization of their result, for gfx950.
 //
 // The producer in front of a transformer block's linears: normalization
 // combined with timestep-dependent scale and shift (TurboT2VA paper,
@@ -17,6 +17,12 @@
 // squares is taken in fp64 in this kernel's order (lane partials, then a
 // butterfly); a different order can move it by a few fp64 ulps, which changes
 // the fp32 r only when r lies within ~2^-50 of an fp32 rounding boundary.
+//
+// The layer form (the fused-kernels paragraph also replaces LayerNorm):
+//   m_i = fl32(mean_k x_ik),  r_i = fl32( 1 / sqrt(var_k x_ik + eps) )  (fp64)
+//   y_ik = bf16( fl32(fl32(fl32(fl32(x_ik - m_i) * r_i) * fl32(1 + scale[b,k])) + shift[b,k]) )
+// with the variance taken over the deviations from the fp64 mean (two passes
+// over the row in ln_rows; the modulate kernels read (m, r) pairs).
 //
 // Three kernels: rms_rows (one wavefront per row, 16-byte loads, fp64
 // partial sums) writes r [B*L]; modulate_bf16 (one wavefront per row) writes
@@ -47,23 +53,40 @@ __device__ __forceinline__ uint32_t bf16_bits(float v) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
 }
 
-__device__ __forceinline__ float modulate(float x, float r, float s, float h) {
-    const float t = x * r;
+// kCenter: the layer normalization's (x - m) * r; else the RMS form x * r.
+template <bool kCenter>
+__device__ __forceinline__ float modulate(float x, float m, float r, float s, float h) {
+    const float c = kCenter ? x - m : x;
+    const float t = c * r;
     const float one_s = 1.0f + s;
     const float u = t * one_s;
     return u + h;
 }
 
 // Two packed bf16 (x, scale, shift words) -> two packed bf16 of y.
-__device__ __forceinline__ uint32_t modulate_word(uint32_t xw, uint32_t sw, uint32_t hw, float r) {
-    const float y0 = modulate(lo_bf16(xw), r, lo_bf16(sw), lo_bf16(hw));
-    const float y1 = modulate(hi_bf16(xw), r, hi_bf16(sw), hi_bf16(hw));
+template <bool kCenter>
+__device__ __forceinline__ uint32_t modulate_word(uint32_t xw, uint32_t sw, uint32_t hw, float m, float r) {
+    const float y0 = modulate<kCenter>(lo_bf16(xw), m, r, lo_bf16(sw), lo_bf16(hw));
+    const float y1 = modulate<kCenter>(hi_bf16(xw), m, r, hi_bf16(sw), hi_bf16(hw));
     return bf16_bits(y0) | (bf16_bits(y1) << 16);
 }
 
-__device__ __forceinline__ u32x4 modulate_chunk(u32x4 x, u32x4 s, u32x4 h, float r) {
-    return u32x4{modulate_word(x.x, s.x, h.x, r), modulate_word(x.y, s.y, h.y, r),
-                 modulate_word(x.z, s.z, h.z, r), modulate_word(x.w, s.w, h.w, r)};
+template <bool kCenter>
+__device__ __forceinline__ u32x4 modulate_chunk(u32x4 x, u32x4 s, u32x4 h, float m, float r) {
+    return u32x4{modulate_word<kCenter>(x.x, s.x, h.x, m, r), modulate_word<kCenter>(x.y, s.y, h.y, m, r),
+                 modulate_word<kCenter>(x.z, s.z, h.z, m, r), modulate_word<kCenter>(x.w, s.w, h.w, m, r)};
+}
+
+// A row's statistics: RMS form r[row]; layer form (m, r) at stats[2 row].
+template <bool kCenter>
+__device__ __forceinline__ void row_stats(const float *__restrict__ st, int64_t row, float &m, float &r) {
+    if (kCenter) {
+        m = st[2 * row];
+        r = st[2 * row + 1];
+    } else {
+        m = 0.0f;
+        r = st[row];
+    }
 }
 
 __device__ __forceinline__ double sq_chunk(u32x4 w) {
@@ -100,7 +123,72 @@ __global__ __launch_bounds__(64 * kRowWaves) void rms_rows_kernel(const uint16_t
     if (lane == 0) r[row] = (float)(1.0 / sqrt(acc / (double)K + eps));
 }
 
+// Layer form: per row m = fl32(mean) and r = fl32(1 / sqrt(var + eps)), the
+// mean and the variance (of the deviations from that mean) in fp64, two
+// passes over the row (the second from cache).
+__device__ __forceinline__ double sum_chunk(u32x4 w) {
+    double a = 0.0;
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a += (double)lo_bf16(v[i]);
+        a += (double)hi_bf16(v[i]);
+    }
+    return a;
+}
+
+__device__ __forceinline__ double dev_chunk(u32x4 w, double mu) {
+    double a = 0.0;
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double l = (double)lo_bf16(v[i]) - mu, h = (double)hi_bf16(v[i]) - mu;
+        a += l * l;
+        a += h * h;
+    }
+    return a;
+}
+
+__global__ __launch_bounds__(64 * kRowWaves) void ln_rows_kernel(const uint16_t *__restrict__ x, int64_t rows,
+                                                                 int64_t K, double eps, float *__restrict__ st) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;  // whole wavefront leaves together
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + row * K);
+    const int64_t chunks = K / 8;
+    double acc = 0.0;
+    int64_t c = lane;
+    for (; c + 3 * 64 < chunks; c += 4 * 64) {  // four loads in flight per lane
+        const u32x4 a = src[c], b = src[c + 64], d = src[c + 128], e = src[c + 192];
+        acc += sum_chunk(a);
+        acc += sum_chunk(b);
+        acc += sum_chunk(d);
+        acc += sum_chunk(e);
+    }
+    for (; c < chunks; c += 64) acc += sum_chunk(src[c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    const double mu = acc / (double)K;
+    double var = 0.0;
+    c = lane;
+    for (; c + 3 * 64 < chunks; c += 4 * 64) {
+        const u32x4 a = src[c], b = src[c + 64], d = src[c + 128], e = src[c + 192];
+        var += dev_chunk(a, mu);
+        var += dev_chunk(b, mu);
+        var += dev_chunk(d, mu);
+        var += dev_chunk(e, mu);
+    }
+    for (; c < chunks; c += 64) var += dev_chunk(src[c], mu);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) var += __shfl_xor(var, o, 64);
+    if (lane == 0) {
+        st[2 * row] = (float)mu;
+        st[2 * row + 1] = (float)(1.0 / sqrt(var / (double)K + eps));
+    }
+}
+
 // y for one row per wavefront.
+template <bool kCenter>
 __global__ __launch_bounds__(64 * kRowWaves) void modulate_bf16_kernel(const uint16_t *__restrict__ x,
                                                                        const float *__restrict__ r, int64_t rows,
                                                                        int64_t L, int64_t K,
@@ -112,13 +200,14 @@ __global__ __launch_bounds__(64 * kRowWaves) void modulate_bf16_kernel(const uin
     const int64_t row = rows - 1 - ((int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6));
     if (row < 0) return;
     const int64_t b = row / L;
-    const float rr = r[row];
+    float mm, rr;
+    row_stats<kCenter>(r, row, mm, rr);
     const u32x4 *src = reinterpret_cast<const u32x4 *>(x + row * K);
     const u32x4 *sc = reinterpret_cast<const u32x4 *>(scale + b * K);
     const u32x4 *sh = reinterpret_cast<const u32x4 *>(shift + b * K);
     u32x4 *dst = reinterpret_cast<u32x4 *>(y + row * K);
     const int64_t chunks = K / 8;
-    for (int64_t c = lane; c < chunks; c += 64) dst[c] = modulate_chunk(src[c], sc[c], sh[c], rr);
+    for (int64_t c = lane; c < chunks; c += 64) dst[c] = modulate_chunk<kCenter>(src[c], sc[c], sh[c], mm, rr);
 }
 
 // One workgroup per 128x128 block of y: each thread holds 64 values (8
@@ -126,6 +215,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void modulate_bf16_kernel(const uin
 // batch entries' scale and shift, then quantizes them as the block quantizer
 // does (absmax on the magnitude bits, wavefront shuffles, LDS across the 4
 // wavefronts, one correctly rounded division per element).
+template <bool kCenter>
 __global__ __launch_bounds__(kBlkThreads) void modulate_quantize_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ r, uint32_t L, int64_t K, int64_t col_blocks,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ shift, int8_t *__restrict__ q,
@@ -154,7 +244,9 @@ __global__ __launch_bounds__(kBlkThreads) void modulate_quantize_kernel(
         const u32x4 sh = *reinterpret_cast<const u32x4 *>(shift + (int64_t)b_first * K + col);
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
-            v[p] = modulate_chunk(v[p], sc, sh, r[row0 + (int64_t)p * kRowsPerPass]);
+            float mm, rr;
+            row_stats<kCenter>(r, row0 + (int64_t)p * kRowsPerPass, mm, rr);
+            v[p] = modulate_chunk<kCenter>(v[p], sc, sh, mm, rr);
             m = max(m, chunk_absmax_bits(v[p]));
         }
     } else {
@@ -164,7 +256,9 @@ __global__ __launch_bounds__(kBlkThreads) void modulate_quantize_kernel(
             const uint32_t b = (uint32_t)row / L;
             const u32x4 sc = *reinterpret_cast<const u32x4 *>(scale + (int64_t)b * K + col);
             const u32x4 sh = *reinterpret_cast<const u32x4 *>(shift + (int64_t)b * K + col);
-            v[p] = modulate_chunk(v[p], sc, sh, r[row]);
+            float mm, rr;
+            row_stats<kCenter>(r, row, mm, rr);
+            v[p] = modulate_chunk<kCenter>(v[p], sc, sh, mm, rr);
             m = max(m, chunk_absmax_bits(v[p]));
         }
     }
@@ -207,25 +301,42 @@ hipError_t launch_rms_rows(const uint16_t *x, int64_t rows, int64_t K, double ep
     return hipGetLastError();
 }
 
-hipError_t launch_modulate_bf16(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
-                                const uint16_t *scale, const uint16_t *shift, uint16_t *y, hipStream_t stream) {
+hipError_t launch_ln_rows(const uint16_t *x, int64_t rows, int64_t K, double eps, float *stats, hipStream_t stream) {
     const int64_t groups = (rows + kRowWaves - 1) / kRowWaves;
     if (groups <= 0) return hipSuccess;
     if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
-    modulate_bf16_kernel<<<dim3((unsigned)groups), dim3(64 * kRowWaves), 0, stream>>>(x, r, rows, L, K, scale,
-                                                                                      shift, y);
+    ln_rows_kernel<<<dim3((unsigned)groups), dim3(64 * kRowWaves), 0, stream>>>(x, rows, K, eps, stats);
     return hipGetLastError();
 }
 
-hipError_t launch_modulate_quantize(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
-                                    const uint16_t *scale, const uint16_t *shift, int8_t *q, float *s,
+hipError_t launch_modulate_bf16(const uint16_t *x, const float *stats, bool center, int64_t rows, int64_t L,
+                                int64_t K, const uint16_t *scale, const uint16_t *shift, uint16_t *y,
+                                hipStream_t stream) {
+    const int64_t groups = (rows + kRowWaves - 1) / kRowWaves;
+    if (groups <= 0) return hipSuccess;
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (center)
+        modulate_bf16_kernel<true><<<dim3((unsigned)groups), dim3(64 * kRowWaves), 0, stream>>>(x, stats, rows, L, K,
+                                                                                                scale, shift, y);
+    else
+        modulate_bf16_kernel<false><<<dim3((unsigned)groups), dim3(64 * kRowWaves), 0, stream>>>(x, stats, rows, L,
+                                                                                                 K, scale, shift, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_modulate_quantize(const uint16_t *x, const float *stats, bool center, int64_t rows, int64_t L,
+                                    int64_t K, const uint16_t *scale, const uint16_t *shift, int8_t *q, float *s,
                                     hipStream_t stream) {
     const int64_t col_blocks = K / kBlock;
     const int64_t tiles = (rows / kBlock) * col_blocks;
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF || rows > 0x7FFFFFFF || L > 0x7FFFFFFF) return hipErrorInvalidValue;
-    modulate_quantize_kernel<<<dim3((unsigned)tiles), dim3(kBlkThreads), 0, stream>>>(
-        x, r, (uint32_t)L, K, col_blocks, scale, shift, q, s);
+    if (center)
+        modulate_quantize_kernel<true><<<dim3((unsigned)tiles), dim3(kBlkThreads), 0, stream>>>(
+            x, stats, (uint32_t)L, K, col_blocks, scale, shift, q, s);
+    else
+        modulate_quantize_kernel<false><<<dim3((unsigned)tiles), dim3(kBlkThreads), 0, stream>>>(
+            x, stats, (uint32_t)L, K, col_blocks, scale, shift, q, s);
     return hipGetLastError();
 }
 

@@ -392,7 +392,8 @@ int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t
     const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
     hipError_t e = w8a8::launch_rms_rows(x, B * L, K, eps, r_ws, stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(w8a8::launch_modulate_bf16(x, r_ws, B * L, L, K, static_cast<const uint16_t *>(scale_bf16),
+    return hip_status(w8a8::launch_modulate_bf16(x, r_ws, false, B * L, L, K,
+                                                 static_cast<const uint16_t *>(scale_bf16),
                                                  static_cast<const uint16_t *>(shift_bf16),
                                                  static_cast<uint16_t *>(y_bf16), stream));
 }
@@ -410,7 +411,46 @@ int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L,
     const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
     hipError_t e = w8a8::launch_rms_rows(x, B * L, K, eps, r_ws, stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(w8a8::launch_modulate_quantize(x, r_ws, B * L, L, K, static_cast<const uint16_t *>(scale_bf16),
+    return hip_status(w8a8::launch_modulate_quantize(x, r_ws, false, B * L, L, K,
+                                                     static_cast<const uint16_t *>(scale_bf16),
+                                                     static_cast<const uint16_t *>(shift_bf16), qx, sx, stream));
+}
+
+int w8a8_layernorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                 const void *shift_bf16, double eps, float *stats_ws, void *y_bf16,
+                                 hipStream_t stream) {
+    const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, stats_ws);
+    if (st != W8A8_OK) return st;
+    if (!y_bf16) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(y_bf16, 16) || !aligned(stats_ws, 8)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(scale_bf16) || !is_device_ptr(shift_bf16) ||
+        !is_device_ptr(stats_ws) || !is_device_ptr(y_bf16))
+        return W8A8_ERR_INVALID_ARG;
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    hipError_t e = w8a8::launch_ln_rows(x, B * L, K, eps, stats_ws, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(w8a8::launch_modulate_bf16(x, stats_ws, true, B * L, L, K,
+                                                 static_cast<const uint16_t *>(scale_bf16),
+                                                 static_cast<const uint16_t *>(shift_bf16),
+                                                 static_cast<uint16_t *>(y_bf16), stream));
+}
+
+int w8a8_layernorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L, int64_t K,
+                                         const void *scale_bf16, const void *shift_bf16, double eps,
+                                         float *stats_ws, int8_t *qx, float *sx, hipStream_t stream) {
+    const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, stats_ws);
+    if (st != W8A8_OK) return st;
+    if (!qx || !sx) return W8A8_ERR_INVALID_ARG;
+    if (!mult128(B * L) || !mult128(K) || !aligned(qx, 16) || !aligned(sx, 4) || !aligned(stats_ws, 8))
+        return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(scale_bf16) || !is_device_ptr(shift_bf16) ||
+        !is_device_ptr(stats_ws) || !is_device_ptr(qx) || !is_device_ptr(sx))
+        return W8A8_ERR_INVALID_ARG;
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    hipError_t e = w8a8::launch_ln_rows(x, B * L, K, eps, stats_ws, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(w8a8::launch_modulate_quantize(x, stats_ws, true, B * L, L, K,
+                                                     static_cast<const uint16_t *>(scale_bf16),
                                                      static_cast<const uint16_t *>(shift_bf16), qx, sx, stream));
 }
 

@@ -51,10 +51,13 @@ hipError_t launch_rope_bf16(const uint16_t *x, int64_t B, int64_t L, int64_t H, 
 // Modulated RMS normalization: r [rows] (fp32), y bf16, and y fused with the
 // 128x128 block quantization (rows and K multiples of 128, rows < 2^31).
 hipError_t launch_rms_rows(const uint16_t *x, int64_t rows, int64_t K, double eps, float *r, hipStream_t stream);
-hipError_t launch_modulate_bf16(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
-                                const uint16_t *scale, const uint16_t *shift, uint16_t *y, hipStream_t stream);
-hipError_t launch_modulate_quantize(const uint16_t *x, const float *r, int64_t rows, int64_t L, int64_t K,
-                                    const uint16_t *scale, const uint16_t *shift, int8_t *q, float *s,
+hipError_t launch_ln_rows(const uint16_t *x, int64_t rows, int64_t K, double eps, float *stats, hipStream_t stream);
+// stats: the RMS form's r per row (center = false) or the layer form's (m, r) per row (center = true)
+hipError_t launch_modulate_bf16(const uint16_t *x, const float *stats, bool center, int64_t rows, int64_t L,
+                                int64_t K, const uint16_t *scale, const uint16_t *shift, uint16_t *y,
+                                hipStream_t stream);
+hipError_t launch_modulate_quantize(const uint16_t *x, const float *stats, bool center, int64_t rows, int64_t L,
+                                    int64_t K, const uint16_t *scale, const uint16_t *shift, int8_t *q, float *s,
                                     hipStream_t stream);
 
 // bf16 fallback on the 256x256-tile kernel: x, w, y 16-byte aligned, K % 64 == 0,

@@ -263,6 +263,26 @@ int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L,
                                        const void *shift_bf16, double eps, float *r_ws, int8_t *qx, float *sx,
                                        hipStream_t stream);
 
+/*
+ * The layer-normalization form of the producer (the fused-kernels paragraph
+ * replaces LayerNorm modules as well as RMSNorm ones), no affine weight; for
+ * row i = b*L + l:
+ *   m_i  = fl32(mean_k x_ik),   r_i = fl32( 1 / sqrt(var_k x_ik + eps) )
+ *          (mean and variance in fp64, the variance over the deviations
+ *          from the fp64 mean)
+ *   y_ik = bf16( fl32( fl32( fl32( fl32(x_ik - m_i) * r_i ) * fl32(1 + scale[b,k]) ) + shift[b,k] ) )
+ * Arguments, layouts and errors as for the RMS entries, except the caller's
+ * workspace stats_ws: 2*B*L floats, 8-byte aligned (else
+ * W8A8_ERR_UNSUPPORTED), left holding (m_i, r_i) per row.  The fused entry
+ * equals, bit for bit, w8a8_quantize_act applied to the bf16 entry's y.
+ */
+int w8a8_layernorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                 const void *shift_bf16, double eps, float *stats_ws, void *y_bf16,
+                                 hipStream_t stream);
+int w8a8_layernorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L, int64_t K,
+                                         const void *scale_bf16, const void *shift_bf16, double eps,
+                                         float *stats_ws, int8_t *qx, float *sx, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Gated residual update (TurboT2VA paper, architecture-aware inference stack,
  * fused-kernels paragraph, which lists gated residual updates among the fused

@@ -42,10 +42,13 @@ hipError_t launch_gemm_bf16_tiled(const uint16_t *, const uint16_t *, const uint
 hipError_t launch_gemm_bf16(const void *, int, const uint16_t *, const uint16_t *, int64_t, int64_t, int64_t, uint16_t *,
                             hipStream_t) { reached("gemm_bf16"); }
 hipError_t launch_rms_rows(const uint16_t *, int64_t, int64_t, double, float *, hipStream_t) { reached("rms_rows"); }
-hipError_t launch_modulate_bf16(const uint16_t *, const float *, int64_t, int64_t, int64_t, const uint16_t *,
+hipError_t launch_modulate_bf16(const uint16_t *, const float *, bool, int64_t, int64_t, int64_t, const uint16_t *,
                                 const uint16_t *, uint16_t *, hipStream_t) { reached("modulate_bf16"); }
-hipError_t launch_modulate_quantize(const uint16_t *, const float *, int64_t, int64_t, int64_t, const uint16_t *,
-                                    const uint16_t *, int8_t *, float *, hipStream_t) { reached("modulate_quantize"); }
+hipError_t launch_modulate_quantize(const uint16_t *, const float *, bool, int64_t, int64_t, int64_t,
+                                    const uint16_t *, const uint16_t *, int8_t *, float *, hipStream_t) {
+    reached("modulate_quantize");
+}
+hipError_t launch_ln_rows(const uint16_t *, int64_t, int64_t, double, float *, hipStream_t) { reached("ln_rows"); }
 }  // namespace w8a8
 
 #define CHECK(cond)                                                                    \
@@ -146,6 +149,14 @@ int main() {
     CHECK(w8a8_linear_gated_residual(p, 0, 256, 256, 256, p, q8, f, nullptr, p, p, 128, pc + (1 << 20), p, 1 << 20,
                                      nullptr, &path) == W8A8_ERR_INVALID_ARG);                    // host memory
     CHECK(path == -7);
+    // modulated layer normalization: the statistics workspace holds (m, r) pairs, 8-byte aligned
+    CHECK(w8a8_layernorm_modulate_bf16(p, 2, 64, 256, p, p, 0.0, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_layernorm_modulate_bf16(p, 2, 64, 256, p, p, 1e-6, f + 1, p, nullptr) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_layernorm_modulate_bf16(p, 2, 64, 256, p, p, 1e-6, f, nullptr, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_layernorm_modulate_quantize_act(p, 2, 100, 256, p, p, 1e-6, f, q8, f, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_layernorm_modulate_quantize_act(p, 2, 128, 256, p, p, 1e-6, f, q8, f, nullptr) ==
+          W8A8_ERR_INVALID_ARG);                                                                  // host memory
     // modulated RMS normalization: eps, sizes, alignment, the fused path's block shape
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, 0.0, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, p, p, -1e-6, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
