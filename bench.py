@@ -26,7 +26,7 @@ the guard's bf16 fallback; and a
 two-stream step (an INT8 linear and a guarded-to-bf16 linear launched on
 two streams at once).
 
-Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|rope|rms|residual
+Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|rope|rms|ln|residual
 launches just that work for --steps iterations (no oracle);
 --copy-calibration runs a plain 1 GiB device copy used to scale the HBM byte
 counters.
@@ -261,7 +261,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "rope", "rms",
-                                       "residual"],
+                                       "ln", "residual"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -333,12 +333,13 @@ def main():
         log(f"--only residual: {args.steps} launches done")
         return
 
-    if args.only == "rms":
+    if args.only in ("rms", "ln"):
         xr, rsc, rsh, yr, rq, rs = rms_buffers(dev)
+        fn = w8a8.rmsnorm_modulate_quantize_act if args.only == "rms" else w8a8.layernorm_modulate_quantize_act
         for _ in range(args.steps):
-            w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)
+            fn(xr, rsc, rsh, 1e-6, rq, rs)
         torch.cuda.synchronize()
-        log(f"--only rms: {args.steps} launches done")
+        log(f"--only {args.only}: {args.steps} launches done")
         return
 
     if args.only in ("gelu_quant", "gelu"):
@@ -595,11 +596,16 @@ def main():
     w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)    # untimed first launches
     w8a8.rmsnorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)
     torch.cuda.synchronize()
-    rt = {"fused": [], "norm": [], "quantize": []}
+    w8a8.layernorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)
+    w8a8.layernorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)
+    torch.cuda.synchronize()
+    rt = {"fused": [], "norm": [], "quantize": [], "ln_fused": [], "ln_norm": []}
     for i in range(args.steps):
         for key, fn in (("fused", lambda: w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)),
                         ("norm", lambda: w8a8.rmsnorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)),
-                        ("quantize", lambda: w8a8.quantize_act(yr.view(RB * RL, RK), rq, rs))):
+                        ("quantize", lambda: w8a8.quantize_act(yr.view(RB * RL, RK), rq, rs)),
+                        ("ln_fused", lambda: w8a8.layernorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)),
+                        ("ln_norm", lambda: w8a8.layernorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr))):
             flush.amax()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -611,6 +617,8 @@ def main():
     del xr, rsc, rsh, yr, rq, rs
     log(f"RMSNorm producer A/B ({RB}x{RL}x{RK}): fused {rms_us['fused']:.1f} us "
         f"({RMS_BYTES / rms_us['fused'] / 1e3:.0f} GB/s algorithmic) vs norm {rms_us['norm']:.1f} + "
+        f"quantize {rms_us['quantize']:.1f} us")
+    log(f"LayerNorm producer A/B: fused {rms_us['ln_fused']:.1f} us vs norm {rms_us['ln_norm']:.1f} + "
         f"quantize {rms_us['quantize']:.1f} us")
 
     # A/B: the post-scale form (per-row / per-channel scales applied once,
@@ -745,6 +753,16 @@ def main():
                                 "unfused_norm_us": round(rms_us["norm"], 2),
                                 "unfused_quantize_us": round(rms_us["quantize"], 2),
                                 "speedup": round((rms_us["norm"] + rms_us["quantize"]) / rms_us["fused"], 3)},
+        "layernorm_producer_ab": {"note": "the same input with the modulated layer normalization (mean and "
+                                          "variance, two passes over each row for its statistics) fused with "
+                                          "the 128x128 block quantize vs the normalization then the quantizer",
+                                  "shape": [RB, RL, RK],
+                                  "fused_us": round(rms_us["ln_fused"], 2),
+                                  "fused_gbs_algorithmic": round(RMS_BYTES / rms_us["ln_fused"] / 1e3, 1),
+                                  "algorithmic_bytes": RMS_BYTES,
+                                  "unfused_norm_us": round(rms_us["ln_norm"], 2),
+                                  "unfused_quantize_us": round(rms_us["quantize"], 2),
+                                  "speedup": round((rms_us["ln_norm"] + rms_us["quantize"]) / rms_us["ln_fused"], 3)},
         "producer_ab": {"note": "MLP producer: exact GELU + 128x128 block quantize of the hidden "
                                 "activation, fused vs GELU then quantize (not part of a step)",
                         "shape": [HM, HK],
