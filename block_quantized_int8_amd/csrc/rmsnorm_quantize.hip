@@ -22,7 +22,8 @@
 //   m_i = fl32(mean_k x_ik),  r_i = fl32( 1 / sqrt(var_k x_ik + eps) )  (fp64)
 //   y_ik = bf16( fl32(fl32(fl32(fl32(x_ik - m_i) * r_i) * fl32(1 + scale[b,k])) + shift[b,k]) )
 // with the variance taken over the deviations from the fp64 mean (two passes
-// over the row in ln_rows; the modulate kernels read (m, r) pairs).
+// over the row in ln_rows, from registers for the common widths; the
+// modulate kernels read (m, r) pairs).
 //
 // Three kernels: rms_rows (one wavefront per row, 16-byte loads, fp64
 // partial sums) writes r [B*L]; modulate_bf16 (one wavefront per row) writes
@@ -187,6 +188,39 @@ __global__ __launch_bounds__(64 * kRowWaves) void ln_rows_kernel(const uint16_t 
     }
 }
 
+// ln_rows for rows of kNc * 512 values (kNc 16-byte chunks per lane): the
+// row stays in registers between the two passes, so x is read once.
+template <int kNc>
+__global__ __launch_bounds__(64 * kRowWaves) void ln_rows_reg_kernel(const uint16_t *__restrict__ x, int64_t rows,
+                                                                     double eps, float *__restrict__ st) {
+    constexpr int64_t K = kNc * 512;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;  // whole wavefront leaves together
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + row * K);
+    u32x4 v[kNc];
+#pragma unroll
+    for (int i = 0; i < kNc; ++i) v[i] = src[lane + 64 * i];
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < kNc; ++i) acc += sum_chunk(v[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    const double mu = acc / (double)K;
+    double var = 0.0;
+#pragma unroll
+    for (int i = 0; i < kNc; ++i) {
+        asm volatile("" : "+v"(v[i]));  // convert again rather than keep 8 doubles per chunk live
+        var += dev_chunk(v[i], mu);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) var += __shfl_xor(var, o, 64);
+    if (lane == 0) {
+        st[2 * row] = (float)mu;
+        st[2 * row + 1] = (float)(1.0 / sqrt(var / (double)K + eps));
+    }
+}
+
 // y for one row per wavefront.
 template <bool kCenter>
 __global__ __launch_bounds__(64 * kRowWaves) void modulate_bf16_kernel(const uint16_t *__restrict__ x,
@@ -305,7 +339,17 @@ hipError_t launch_ln_rows(const uint16_t *x, int64_t rows, int64_t K, double eps
     const int64_t groups = (rows + kRowWaves - 1) / kRowWaves;
     if (groups <= 0) return hipSuccess;
     if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
-    ln_rows_kernel<<<dim3((unsigned)groups), dim3(64 * kRowWaves), 0, stream>>>(x, rows, K, eps, stats);
+    const dim3 grid((unsigned)groups), block(64 * kRowWaves);
+    switch (K) {  // rows that fit in registers: one read of x
+    case 1024: ln_rows_reg_kernel<2><<<grid, block, 0, stream>>>(x, rows, eps, stats); break;
+    case 2048: ln_rows_reg_kernel<4><<<grid, block, 0, stream>>>(x, rows, eps, stats); break;
+    case 3072: ln_rows_reg_kernel<6><<<grid, block, 0, stream>>>(x, rows, eps, stats); break;
+    case 4096: ln_rows_reg_kernel<8><<<grid, block, 0, stream>>>(x, rows, eps, stats); break;
+    case 5120: ln_rows_reg_kernel<10><<<grid, block, 0, stream>>>(x, rows, eps, stats); break;
+    case 6144: ln_rows_reg_kernel<12><<<grid, block, 0, stream>>>(x, rows, eps, stats); break;
+    case 8192: ln_rows_reg_kernel<16><<<grid, block, 0, stream>>>(x, rows, eps, stats); break;
+    default: ln_rows_kernel<<<grid, block, 0, stream>>>(x, rows, K, eps, stats); break;
+    }
     return hipGetLastError();
 }
 

@@ -39,7 +39,10 @@ def gpu_y(x, L, sc, sh, eps):
     return bf16_bits(y).reshape(x.shape)
 
 
-@pytest.mark.parametrize("B,L,K,eps", [(2, 300, 512, 1e-6), (3, 77, 136, 1e-6), (1, 5, 8, 0.5), (4, 96, 4096, 1e-5)])
+@pytest.mark.parametrize("B,L,K,eps", [(2, 300, 512, 1e-6), (3, 77, 136, 1e-6), (1, 5, 8, 0.5), (4, 96, 4096, 1e-5),
+                                       # the widths whose rows stay in registers for the statistics
+                                       (2, 64, 1024, 1e-6), (1, 40, 2048, 1e-6), (1, 33, 3072, 1e-6),
+                                       (1, 17, 5120, 1e-6), (1, 16, 6144, 1e-6), (1, 13, 8192, 1e-6)])
 def test_bf16_output_bit_exact(B, L, K, eps):
     x = off_centre(B * 1000 + L, B * L, K)
     sc = random_bf16(K + 1, (B, K), 0.3)
