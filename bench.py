@@ -690,7 +690,9 @@ def main():
         "quantize_us": round(quant_ms * 1e3, 2),
         "roofline": {"bound": "mfma", "kernel": "gemm_i8_blockscale",
                      "achieved": round(gemm_tops, 1), "peak": round(PEAK_INT8_TOPS, 1),
-                     "unit": "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "unit_note": "int8 operations (a multiply-add counts 2) per second, 1e12, against the "
+                                  "dense int8 MFMA peak",
                      "traffic": traffic,
                      "algorithmic_bytes": GEMM_BYTES, "ops_per_launch": GEMM_OPS},
         "roofline_quantize": {"bound": "hbm", "kernel": "quantize_block",
