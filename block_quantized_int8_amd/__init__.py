@@ -329,6 +329,8 @@ def gated_residual(h: torch.Tensor, o: torch.Tensor, gate: torch.Tensor, out=Non
     if out is None:
         out = torch.empty_like(o)
     _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out must have as many elements as o")
     check("w8a8_gated_residual", lib().w8a8_gated_residual(_ptr(h), _ptr(o), _ptr(gate), M // L, L, N, _ptr(out),
                                                            _stream(o.device)))
     return out
@@ -337,32 +339,46 @@ def gated_residual(h: torch.Tensor, o: torch.Tensor, gate: torch.Tensor, out=Non
 def gemm_blockscale_gated_residual(qx, sx, qw, sw, h, gate, bias=None, out=None):
     """``gated_residual(h, gemm_blockscale(qx, sx, qw, sw, bias), gate)`` with
     the update in the GEMM's epilogue; ``out`` may be ``h`` (in place)."""
-    M, K = qx.shape
-    N = qw.shape[0]
+    M, N, K, out = _gemm_operands(qx, sx, qw, sw, bias, out, True)
     L = _residual_args(h, gate, M, N)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
     check("w8a8_gemm_blockscale_gated_residual",
           lib().w8a8_gemm_blockscale_gated_residual(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(bias), M, N, K,
                                                     _ptr(h), _ptr(gate), L, _ptr(out), _stream(qx.device)))
     return out
 
 
-def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):
-    """INT8 GEMM with per-K-block dequantization -> bf16 [M, N]."""
+def _gemm_operands(qx, sx, qw, sw, bias, out, block_scales: bool):
+    """Check the quantized operands, bias and output of a GEMM call (sizes
+    included, so that no kernel can be pointed past a buffer) -> (M, N, K, out)."""
     _need_cuda("qx", qx, torch.int8)
     _need_cuda("qw", qw, torch.int8)
     _need_cuda("sx", sx, torch.float32)
     _need_cuda("sw", sw, torch.float32)
+    if qx.dim() != 2 or qw.dim() != 2:
+        raise ValueError("qx and qw must be 2-D")
     M, K = qx.shape
     N = qw.shape[0]
     if qw.shape[1] != K:
         raise ValueError("qx and qw disagree on K")
+    want_sx, want_sw = ((-(-M // BLOCK)) * (-(-K // BLOCK)), (-(-N // BLOCK)) * (-(-K // BLOCK))) if block_scales \
+        else (M, N)
+    if sx.numel() != want_sx or sw.numel() != want_sw:
+        raise ValueError("scale grids do not match the operands")
     if bias is not None:
         _need_cuda("bias", bias, torch.bfloat16)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
     _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out must have M x N elements")
+    return M, N, K, out
+
+
+def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):
+    """INT8 GEMM with per-K-block dequantization -> bf16 [M, N]."""
+    M, N, K, out = _gemm_operands(qx, sx, qw, sw, bias, out, True)
     check("w8a8_gemm_blockscale",
           lib().w8a8_gemm_blockscale(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(bias), M, N, K,
                                      _ptr(out), _stream(qx.device)))
@@ -392,9 +408,15 @@ def _guarded(fn_name, ws_bytes, x, w, qw, sw, bias, out, workspace):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out must have M x N elements")
+    if bias is not None and bias.numel() != N:
+        raise ValueError("bias must have N elements")
     need = ws_bytes(M, K) if qw is not None else 0
-    if need and (workspace is None or workspace.numel() < need):
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if need:
+        _need_cuda("workspace", workspace)
     path = ctypes.c_int(-1)
     check(fn_name,
           getattr(lib(), fn_name)(_ptr(x2), _DTYPES[x.dtype], M, K, N, _ptr(w), _ptr(qw), _ptr(sw),
@@ -433,19 +455,7 @@ def quantize_rows(x: torch.Tensor, q=None, s=None):
 
 def gemm_postscale(qx, sx, qw, sw, bias=None, out=None):
     """Post-scale INT8 GEMM (int32 over all of K, scales once) -> bf16 [M, N]."""
-    _need_cuda("qx", qx, torch.int8)
-    _need_cuda("qw", qw, torch.int8)
-    _need_cuda("sx", sx, torch.float32)
-    _need_cuda("sw", sw, torch.float32)
-    M, K = qx.shape
-    N = qw.shape[0]
-    if qw.shape[1] != K or sx.numel() != M or sw.numel() != N:
-        raise ValueError("operand shapes disagree")
-    if bias is not None:
-        _need_cuda("bias", bias, torch.bfloat16)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
-    _need_cuda("out", out, torch.bfloat16)
+    M, N, K, out = _gemm_operands(qx, sx, qw, sw, bias, out, False)
     check("w8a8_gemm_postscale",
           lib().w8a8_gemm_postscale(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(bias), M, N, K,
                                     _ptr(out), _stream(qx.device)))
@@ -594,6 +604,8 @@ class W8A8Linear(torch.nn.Module):
         if out is None:
             out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
         _need_cuda("out", out, torch.bfloat16)
+        if out.numel() != M * N:
+            raise ValueError("out must have the output's M x N elements")
         need = workspace_bytes(M, K) if self.qweight is not None else 0
         if need and (self._workspace is None or self._workspace.numel() < need
                      or self._workspace.device != x.device):
