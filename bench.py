@@ -217,6 +217,70 @@ def residual_buffers(dev):
     return h, g, torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
 
+def block_slice_ab(w8a8, dev, steps):
+    """One transformer block's W8A8 work, attention excluded: modulated
+    RMSNorm -> Q/K/V projection group -> split rotary embedding and INT8 Q/K
+    -> output projection + gated residual -> modulated RMSNorm -> MLP up ->
+    GELU -> MLP down + gated residual.  Fused: each producer in the next
+    quantizer, each residual update in the GEMM epilogue; unfused: every step
+    on its own through bf16 tensors.  V stands in for the attention output.
+    Returns the mean time per block of each chain (us)."""
+    import numpy as np
+    import torch
+    from block_quantized_int8_amd.workloads import random_bf16, rope_tables
+    B, L, D, H, HD, F = RB, RL, RK, 32, 128, 16384
+    Mb = B * L
+    t = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    h0 = t(random_bf16(200, (Mb, D), 2.0))
+    mod = [t(random_bf16(201 + i, (B, D), 0.3)) for i in range(4)]      # scale/shift of the two norms
+    gates = [t(random_bf16(205 + i, (B, D), 0.5)) for i in range(2)]
+    qkv = w8a8.W8A8Linear(t(random_bf16(207, (3 * D, D), 0.02)))
+    out_p = w8a8.W8A8Linear(t(random_bf16(208, (D, D), 0.02)))
+    up = w8a8.W8A8Linear(t(random_bf16(209, (F, D), 0.02)))
+    down = w8a8.W8A8Linear(t(random_bf16(210, (D, F), 0.02)))
+    cs, sn = (torch.from_numpy(a).to(dev) for a in rope_tables(L, HD))
+    h = torch.empty_like(h0)
+    h1 = torch.empty_like(h0)
+    qq = torch.empty((B, H, L, HD), dtype=torch.int8, device=dev)
+    sq = torch.empty((B, H, L // 128), dtype=torch.float32, device=dev)
+    kq, ks = torch.empty_like(qq), torch.empty_like(sq)
+    qg = torch.empty((Mb, F), dtype=torch.int8, device=dev)
+    sg = torch.empty((Mb // 128, F // 128), dtype=torch.float32, device=dev)
+
+    def fused():
+        y = qkv.forward_modulated(h.view(B, L, D), mod[0], mod[1]).view(B, L, 3 * D)
+        w8a8.rope_quantize_qk(y[:, :, :D], H, cs, sn, qq, sq)
+        w8a8.rope_quantize_qk(y[:, :, D:2 * D], H, cs, sn, kq, ks)
+        out_p.forward_gated_residual(y[:, :, 2 * D:], h, gates[0], out=h1)
+        u = up.forward_modulated(h1.view(B, L, D), mod[2], mod[3])
+        w8a8.gelu_quantize_act(u.view(Mb, F), qg, sg)
+        w8a8.gemm_blockscale_gated_residual(qg, sg, down.qweight, down.wscale, h1, gates[1], out=h)
+
+    def unfused():
+        y = qkv(w8a8.rmsnorm_modulate_bf16(h.view(B, L, D), mod[0], mod[1])).view(B, L, 3 * D)
+        w8a8.quantize_qk(w8a8.rope_bf16(y[:, :, :D], H, cs, sn), H, qq, sq)
+        w8a8.quantize_qk(w8a8.rope_bf16(y[:, :, D:2 * D], H, cs, sn), H, kq, ks)
+        w8a8.gated_residual(h, out_p(y[:, :, 2 * D:].reshape(Mb, D)), gates[0], out=h1)
+        u = up(w8a8.rmsnorm_modulate_bf16(h1.view(B, L, D), mod[2], mod[3]))
+        o = down(w8a8.gelu_bf16(u))
+        w8a8.gated_residual(h1, o.view(Mb, D), gates[1], out=h)
+
+    res = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        h.copy_(h0)
+        fn()                                   # untimed first launches
+        torch.cuda.synchronize()
+        h.copy_(h0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / steps * 1e3
+    return res
+
+
 def rope_tables_dev(dev):
     import torch
     from block_quantized_int8_amd.workloads import rope_tables
@@ -621,6 +685,12 @@ def main():
     log(f"LayerNorm producer A/B: fused {rms_us['ln_fused']:.1f} us vs norm {rms_us['ln_norm']:.1f} + "
         f"quantize {rms_us['quantize']:.1f} us")
 
+    # a transformer block's W8A8 work (attention itself excluded), 4 x 8192
+    # tokens x 4096, 32 heads of 128, MLP 16384: every fusion of the library
+    # in place vs the same steps unfused
+    blk_us = block_slice_ab(w8a8, dev, args.steps)
+    log(f"block slice: fused {blk_us['fused']:.1f} us vs unfused {blk_us['unfused']:.1f} us per block")
+
     # A/B: the post-scale form (per-row / per-channel scales applied once,
     # INT32 over all of K) on the same inputs and shape
     qwp, swp = w8a8.quantize_rows(w)
@@ -732,6 +802,14 @@ def main():
                               "unfused_update_us": round(res_us["update"], 2),
                               "update_gbs": round(RES_UPDATE_BYTES / res_us["update"] / 1e3, 1),
                               "speedup": round((res_us["gemm"] + res_us["update"]) / res_us["fused"], 3)},
+        "block_slice_ab": {"note": "one transformer block's W8A8 work, attention excluded (4 x 8192 tokens x 4096, "
+                                   "32 heads of 128, MLP 16384): modulated RMSNorm -> Q/K/V group -> rotary + INT8 "
+                                   "Q/K -> output projection + gated residual -> modulated RMSNorm -> MLP up -> "
+                                   "GELU -> MLP down + gated residual; fused = every producer in the next quantizer "
+                                   "and every residual update in the GEMM epilogue, unfused = the same steps through "
+                                   "bf16 tensors; V stands in for the attention output (not part of a step)",
+                           "fused_us": round(blk_us["fused"], 1), "unfused_us": round(blk_us["unfused"], 1),
+                           "speedup": round(blk_us["unfused"] / blk_us["fused"], 3)},
         "rope_qk_ab": {"note": "split-halves rotary embedding fused into the INT8 Q/K quantizer vs rotation "
                                "to bf16 then quantization, per Q or K tensor of the video self-attention "
                                "(not part of a step); tables fp32 [tokens, head_dim/2]",
