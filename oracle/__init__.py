@@ -52,11 +52,16 @@ def lib():
         L.oracle_rope.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
         L.oracle_gated_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
         L.oracle_layernorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
+        L.oracle_quantize_v_fp8.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
+        L.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+        L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_f64.restype = ctypes.c_double
         for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
                   "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
                   "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
                   "oracle_quantize_qk", "oracle_rmsnorm_modulate", "oracle_rope",
-                  "oracle_gated_residual", "oracle_layernorm_modulate"):
+                  "oracle_gated_residual", "oracle_layernorm_modulate", "oracle_quantize_v_fp8"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -286,3 +291,26 @@ def gated_residual(h_bf16: np.ndarray, o_bf16: np.ndarray, gate_bf16: np.ndarray
     y = np.empty((R, N), np.uint16)
     _check(lib().oracle_gated_residual(_ptr(h), _ptr(o), _ptr(g), R // L, L, N, _ptr(y)), "gated_residual")
     return y
+
+
+def f32_to_e4m3(v: float) -> int:
+    """One finite float -> its FP8 E4M3 code (nearest, ties to even; beyond 448: NaN)."""
+    return int(lib().oracle_f32_to_e4m3(float(v)))
+
+
+def e4m3_to_f64(code: int) -> float:
+    return float(lib().oracle_e4m3_to_f64(int(code)))
+
+
+def quantize_v_fp8(x_bf16: np.ndarray, B: int, L: int, H: int, D: int, ld: int):
+    """Attention V in FP8: rows b*L + l of width ld, head h at columns h*D ..;
+    per (b, h) and 128-token block s = fl32(max|x| / 448), codes E4M3(fl32(x / s))
+    -> (q uint8 [B, H, L, D], s fp32 [B, H, ceil(L/128)])."""
+    x = _c(x_bf16, np.uint16)
+    if x.size != B * L * ld:
+        raise ValueError("x must hold B*L rows of ld values")
+    nblk = -(-L // 128)
+    q = np.empty((B, H, L, D), np.uint8)
+    s = np.empty((B, H, nblk), np.float32)
+    _check(lib().oracle_quantize_v_fp8(_ptr(x), B, L, H, D, ld, _ptr(q), _ptr(s)), "quantize_v_fp8")
+    return q, s

@@ -26,6 +26,8 @@
  *   - INT8 query/key of the sparse attention, block rule over 128 tokens x
  *       head dim, rearranged sequence-major -> head-major: TurboT2VA paper,
  *       same section, sparse-attention paragraph.
+ *   - attention V in FP8 E4M3 per block of 128 tokens x the head dim, beside
+ *       the INT8 Q/K: same section, sparse-attention paragraph (FP8 values).
  *   - modulated layer normalization (mean and variance, no affine weight):
  *       same section, fused-kernels paragraph (LayerNorm replaced).
  *   - gated residual update h + g * o of a linear's output: same section,
@@ -368,6 +370,80 @@ int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64
                 }
                 q[(bh * L + l) * D + d] = out;
             }
+    }
+    return OR_OK;
+}
+
+/*
+ * FP8 E4M3 (the OCP 8-bit floating-point format: 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN, largest finite
+ * 448, subnormals down to 2^-9) from a finite float, rounded to nearest, ties
+ * to the even code.  Values whose rounding would exceed 448 give NaN (0x7F
+ * with the sign), as no finite code is nearer.
+ */
+uint8_t oracle_f32_to_e4m3(float v) {
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs((double)v);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);          /* a = f * 2^e, 0.5 <= f < 1: leading bit 2^(e-1) */
+    int E = e - 1;
+    if (E < -6) E = -6;          /* subnormal range: quantum 2^-9 */
+    const double quantum = ldexp(1.0, E - 3);
+    double q = a / quantum;      /* exact: scaling by a power of two */
+    double f = floor(q);
+    const double d = q - f;
+    if (d > 0.5 || (d == 0.5 && fmod(f, 2.0) == 1.0)) f += 1.0;
+    /* f in [8, 16] for normals (16 carries into the next binade), [0, 8] for subnormals */
+    int code;
+    if (E == -6 && f < 8.0)
+        code = (int)f;                                  /* subnormal (or rounded up to 2^-6: f == 8) */
+    else if (f >= 16.0)
+        code = ((E + 1 + 7) << 3);                      /* carried: mantissa 0 of the next binade */
+    else
+        code = ((E + 7) << 3) | ((int)f - 8);
+    if (code > 0x7E) return (uint8_t)(sign | 0x7F);     /* beyond 448 */
+    return (uint8_t)(sign | code);
+}
+
+/* Value of an E4M3 code (NaN for S.1111.111). */
+double oracle_e4m3_to_f64(uint8_t c) {
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return s ? -v : v;
+}
+
+/*
+ * Attention V in FP8 (TurboT2VA paper, architecture-aware inference stack,
+ * sparse-attention paragraph: the value aggregation takes FP8 values while Q
+ * and K are INT8), in the same layout and blocks as oracle_quantize_qk:
+ * per (b, h) and block of 128 tokens x D, a = max |x|, s = fl32(a / 448),
+ * code = E4M3(fl32(x / s)) (an all-zero block: s = 0, codes 0).  Codes go to
+ * q[((b*H + h)*L + l)*D + d] (head-major), scales to s[(b*H + h)*nblk + j].
+ */
+int oracle_quantize_v_fp8(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, uint8_t *q,
+                          float *s) {
+    if (!x || !q || !s || B <= 0 || L <= 0 || H <= 0 || D <= 0 || ld < H * D) return OR_ERR_ARG;
+    const int64_t nblk = (L + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t task = 0; task < B * H * nblk; ++task) {
+        const int64_t bh = task / nblk, j = task % nblk;
+        const int64_t b = bh / H, h = bh % H;
+        const int64_t l0 = j * ORACLE_BLOCK;
+        const int64_t l1 = l0 + ORACLE_BLOCK < L ? l0 + ORACLE_BLOCK : L;
+        float a = 0.0f;
+        for (int64_t l = l0; l < l1; ++l)
+            for (int64_t d = 0; d < D; ++d) {
+                float v = fabsf(oracle_bf16_to_f32(x[(b * L + l) * ld + h * D + d]));
+                if (v > a) a = v;
+            }
+        const float sc = a / 448.0f;
+        s[bh * nblk + j] = sc;
+        for (int64_t l = l0; l < l1; ++l)
+            for (int64_t d = 0; d < D; ++d)
+                q[(bh * L + l) * D + d] =
+                    a != 0.0f ? oracle_f32_to_e4m3(oracle_bf16_to_f32(x[(b * L + l) * ld + h * D + d]) / sc) : 0;
     }
     return OR_OK;
 }

@@ -20,7 +20,8 @@ the definitions:
   per-output-channel max(max-abs, 1e-4) / 127, integer sum over all of K,
   scales and bias once at the end);
 * INT8 attention Q/K (TurboT2VA paper, sparse-attention paragraph): the
-  block rule over 128 tokens x the head dimension, per batch and head;
+  block rule over 128 tokens x the head dimension, per batch and head; V in
+  FP8 E4M3 over the same blocks (same paragraph: FP8 values);
 * the modulated RMS and layer normalizations, the split-halves rotary
   embedding and the gated residual update (TurboT2VA paper, fused-kernels
   paragraph).
@@ -185,6 +186,55 @@ def quantize_qk(x_bits: np.ndarray, B: int, L: int, H: int, D: int, ld: int):
                 sc = np.float32(a / np.float32(127.0))
                 s[b, h, j] = sc
                 q[b, h, j * BLOCK:j * BLOCK + blk.shape[0]] = _codes(blk, sc)
+    return q, s
+
+
+# ------------------------------------------------------------ attention V, FP8
+
+def _e4m3_table():
+    """(value, code) of every finite non-negative E4M3 code, by its definition."""
+    out = []
+    for c in range(0x7F):            # 0x7F is NaN
+        e, m = c >> 3, c & 7
+        v = math.ldexp(m, -9) if e == 0 else math.ldexp(8 + m, e - 10)
+        out.append((v, c))
+    return out
+
+
+_E4M3 = _e4m3_table()
+
+
+def e4m3_code(v: float) -> int:
+    """Nearest finite E4M3 code by search over all codes, ties to the even
+    code; NaN (0x7F) beyond 464, where the next step up (480, not a finite
+    code) is nearer than 448 (at 464 itself the tie goes to 448's even code)."""
+    sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+    a = abs(v)
+    if a > 464.0:
+        return sign | 0x7F
+    best = min(_E4M3, key=lambda vc: (abs(vc[0] - a), vc[1] & 1))
+    return sign | best[1]
+
+
+def quantize_v_fp8(x_bits: np.ndarray, B: int, L: int, H: int, D: int, ld: int):
+    """Per (b, h) and block of 128 tokens x D: s = fl32(max|x| / 448), codes
+    E4M3(fl32(x / s)); head-major [B, H, L, D] codes and [B, H, blocks] scales."""
+    x = np.asarray(x_bits, np.uint16).reshape(B * L, ld)
+    nblk = -(-L // BLOCK)
+    q = np.zeros((B, H, L, D), np.uint8)
+    s = np.zeros((B, H, nblk), np.float32)
+    for b in range(B):
+        for h in range(H):
+            head = bf16_to_f64(x[b * L:(b + 1) * L, h * D:(h + 1) * D]).astype(np.float32)
+            for j in range(nblk):
+                blk = head[j * BLOCK:min((j + 1) * BLOCK, L)]
+                a = np.float32(np.max(np.abs(blk)))
+                sc = np.float32(a / np.float32(448.0))
+                s[b, h, j] = sc
+                if a == 0:
+                    continue
+                quo = (blk / sc).astype(np.float32)
+                q[b, h, j * BLOCK:j * BLOCK + blk.shape[0]] = np.vectorize(lambda v: e4m3_code(float(v)))(quo)
     return q, s
 
 

@@ -6,7 +6,9 @@
  * Buffers are allocated at their exact sizes so that an overrun is caught.
  */
 #include <stdint.h>
+#include <math.h>
 #include <stdio.h>
+#include <string.h>
 #include <stdlib.h>
 
 int oracle_quantize_block(const uint16_t *x, int64_t rows, int64_t cols, int8_t *q, float *s);
@@ -24,6 +26,10 @@ int oracle_linear_postscale_rows(const int8_t *qx, const float *sx, const int8_t
 int oracle_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, int8_t *q,
                        float *s);
 int oracle_route(int x_dtype, int64_t M, int64_t K, int64_t N, int has_qweight);
+int oracle_quantize_v_fp8(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, uint8_t *q,
+                          float *s);
+uint8_t oracle_f32_to_e4m3(float v);
+double oracle_e4m3_to_f64(uint8_t c);
 int oracle_layernorm_modulate(const uint16_t *x, int64_t B, int64_t L, int64_t K, const uint16_t *scale,
                               const uint16_t *shift, double eps, uint16_t *y, float *stats_out);
 int oracle_gated_residual(const uint16_t *h, const uint16_t *o, const uint16_t *gate, int64_t B, int64_t L,
@@ -98,6 +104,19 @@ int main(void) {
     float *qs = xmalloc(sizeof(float) * B * H * nblk);
     CHECK(oracle_quantize_qk(qkx, B, L, H, D, ld, qq, qs) == 0);
     CHECK(oracle_quantize_qk(qkx, B, L, H, D, H * D - 1, qq, qs) != 0);
+
+    /* V in FP8 on the same padded rows; every code decoded and every bf16 pattern encoded */
+    uint8_t *vq = xmalloc(B * H * L * D);
+    CHECK(oracle_quantize_v_fp8(qkx, B, L, H, D, ld, vq, qs) == 0);
+    CHECK(oracle_quantize_v_fp8(qkx, B, L, H, D, H * D - 1, vq, qs) != 0);
+    for (int c = 0; c < 256; ++c) (void)oracle_e4m3_to_f64((uint8_t)c);
+    for (int i = 0; i < 65536; ++i) {
+        uint32_t u = (uint32_t)i << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        if (isfinite(f)) (void)oracle_f32_to_e4m3(f);
+    }
+    free(vq);
 
     /* split rotary embedding on the same padded rows */
     float *rc = xmalloc(sizeof(float) * L * (D / 2)), *rs = xmalloc(sizeof(float) * L * (D / 2));
