@@ -30,7 +30,8 @@ concatenated output channels and returns one view per projection;
 ``quantize_qk(x, heads)`` turns such a Q or K view (sequence-major) into
 head-major INT8 codes with one scale per 128 tokens of each head;
 ``rope_bf16(x, heads, cos, sin)`` applies the split-halves rotary embedding
-and ``rope_quantize_qk(x, heads, cos, sin)`` fuses it into that quantizer.
+and ``rope_quantize_qk(x, heads, cos, sin)`` fuses it into that quantizer;
+``quantize_v_fp8(x, heads)`` gives V the same treatment in FP8 E4M3.
 
 Consumer fused with the GEMM: ``gated_residual(h, o, gate)`` (h + gate * o),
 ``gemm_blockscale_gated_residual`` (the update in the block GEMM's epilogue)
@@ -374,6 +375,25 @@ def _gemm_operands(qx, sx, qw, sw, bias, out, block_scales: bool):
     if out.numel() != M * N:
         raise ValueError("out must have M x N elements")
     return M, N, K, out
+
+
+def quantize_v_fp8(x: torch.Tensor, heads: int, q=None, s=None):
+    """Attention V in FP8 E4M3: ``x`` as for ``quantize_qk`` -> (q uint8
+    [B, H, L, D] holding E4M3 bit patterns, s fp32 [B, H, ceil(L/128)]),
+    one scale (max-abs / 448) per block of 128 tokens of each head."""
+    x3, B, L, D, ld = _qk_view(x, heads)
+    nblk = -(-L // BLOCK)
+    if q is None:
+        q = torch.empty((B, heads, L, D), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((B, heads, nblk), dtype=torch.float32, device=x.device)
+    _need_cuda("q", q, torch.uint8)
+    _need_cuda("s", s, torch.float32)
+    if q.numel() != B * heads * L * D or s.numel() != B * heads * nblk:
+        raise ValueError("output buffers have the wrong size")
+    check("w8a8_quantize_v_fp8", lib().w8a8_quantize_v_fp8(_ptr(x3), B, L, heads, D, ld, _ptr(q), _ptr(s),
+                                                           _stream(x.device)))
+    return (q, s) if x.dim() == 3 else (q[0], s[0])
 
 
 def gemm_blockscale(qx, sx, qw, sw, bias=None, out=None):

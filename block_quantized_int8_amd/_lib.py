@@ -27,6 +27,7 @@ EXPORTS = (
     "w8a8_rmsnorm_modulate_bf16", "w8a8_rmsnorm_modulate_quantize_act", "w8a8_rope_bf16",
     "w8a8_rope_quantize_qk", "w8a8_gated_residual", "w8a8_gemm_blockscale_gated_residual",
     "w8a8_linear_gated_residual", "w8a8_layernorm_modulate_bf16", "w8a8_layernorm_modulate_quantize_act",
+    "w8a8_quantize_v_fp8",
 )
 POSTSCALE_MAX_K = 133120
 BLOCK_MAX_K = 4194304
@@ -72,6 +73,7 @@ def lib():
     L.w8a8_gelu_bf16.argtypes = [_P, _I64, _P, _P]
     L.w8a8_gelu_quantize_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
     L.w8a8_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
+    L.w8a8_quantize_v_fp8.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.w8a8_rope_bf16.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]
     L.w8a8_rope_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
     L.w8a8_gated_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P]
@@ -93,7 +95,7 @@ def lib():
               "w8a8_gelu_bf16", "w8a8_gelu_quantize_act", "w8a8_quantize_qk", "w8a8_rope_bf16",
               "w8a8_rope_quantize_qk", "w8a8_rmsnorm_modulate_bf16", "w8a8_rmsnorm_modulate_quantize_act",
               "w8a8_gated_residual", "w8a8_gemm_blockscale_gated_residual", "w8a8_linear_gated_residual",
-              "w8a8_layernorm_modulate_bf16", "w8a8_layernorm_modulate_quantize_act"):
+              "w8a8_layernorm_modulate_bf16", "w8a8_layernorm_modulate_quantize_act", "w8a8_quantize_v_fp8"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

@@ -33,7 +33,56 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;  // accelerator complex dies of gfx950, each with its own L2
 
-template <int D>
+// ---- FP8 values (the same blocks and layout, codes in FP8 E4M3)
+//
+// The sparse attention takes V in FP8 beside the INT8 Q and K (TurboT2VA
+// paper, sparse-attention paragraph).  Per block s = fl32(a / 448) and
+// code = E4M3(fl32(x / s)), the OCP format (bias 7, largest finite 448),
+// nearest with ties to even: v_cvt_pk_fp8_f32 rounds an fp32 value that way.
+// The quotient comes from quant_math.h's corrected reciprocal product
+// (checked on the CPU for every pair of bf16 values 0 <= x <= a with
+// s = fl32(a / 448), prescaled below 2^-60: it is not always the correctly
+// rounded fp32 quotient, but its E4M3 code always equals that quotient's).
+// A block's max-abs element can give a quotient a hair above 448; it is
+// clamped to 448, which is also where E4M3 rounding takes anything below 464.
+constexpr float kFp8Max = 448.0f;
+
+__device__ __forceinline__ float quotient(float x, float ss, float r) {
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(-q0, ss, x);
+    return __builtin_fmaf(e, r, q0);
+}
+
+// Four E4M3 codes from two words of packed bf16 (elements 0-3, little endian).
+template <bool kScaled>
+__device__ __forceinline__ uint32_t fp8_word(uint32_t lo, uint32_t hi, float f, float ss, float r) {
+    float v[4] = {__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u), __uint_as_float(hi << 16),
+                  __uint_as_float(hi & 0xFFFF0000u)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (kScaled) v[i] *= f;
+        // the corrected product turns x = -0 into +0; E4M3 keeps the sign of a zero quotient
+        v[i] = __builtin_copysignf(__builtin_fminf(__builtin_fmaxf(quotient(v[i], ss, r), -kFp8Max), kFp8Max), v[i]);
+    }
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+}
+
+template <bool kScaled>
+__device__ __forceinline__ u32x2 fp8_chunk(u32x4 w, float f, float ss, float r) {
+    return u32x2{fp8_word<kScaled>(w.x, w.y, f, ss, r), fp8_word<kScaled>(w.z, w.w, f, ss, r)};
+}
+
+// INT8 codes (the Q/K rule) or E4M3 codes (V) of one chunk.
+template <bool kFp8, bool kScaled>
+__device__ __forceinline__ u32x2 block_codes(u32x4 w, float f, float ss, float r) {
+    if constexpr (kFp8)
+        return fp8_chunk<kScaled>(w, f, ss, r);
+    else
+        return code_chunk<kScaled>(w, f, ss, r);
+}
+
+template <int D, bool kFp8>
 __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(const uint16_t *__restrict__ x, int64_t L,
                                                               int64_t H, int64_t ld, int64_t nblk,
                                                               int8_t *__restrict__ q, float *__restrict__ s) {
@@ -67,9 +116,10 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(const uint16_t *_
     __syncthreads();
     m = __builtin_amdgcn_readfirstlane(max(max(red[0], red[1]), max(red[2], red[3])));  // uniform
 
-    const float sc = __uint_as_float(m << 16) / 127.0f;  // IEEE division, correctly rounded
+    const float sc = __uint_as_float(m << 16) / (kFp8 ? kFp8Max : 127.0f);  // IEEE division, correctly rounded
     if (t == 0) s[task] = sc;
-    // an all-zero block (every value +-0) gets codes 0 from divisor 1
+    // an all-zero block (every value +-0) gets codes 0 from divisor 1 (INT8),
+    // or is written as zeros (E4M3 would keep the sign of a -0)
     const bool scaled = m != 0 && sc < kTinyScale;
     const float f = scaled ? kPrescale : 1.0f;
     const float ss = m == 0 ? 1.0f : sc * f;
@@ -79,7 +129,9 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(const uint16_t *_
     for (int p = 0; p < kPasses; ++p) {
         if (l0 + p * kRowsPerPass < L)
             *reinterpret_cast<u32x2 *>(dst + (int64_t)p * kRowsPerPass * D) =
-                scaled ? code_chunk<true>(v[p], f, ss, r) : code_chunk<false>(v[p], 1.0f, ss, r);
+                (kFp8 && m == 0) ? u32x2{0u, 0u}
+                : scaled         ? block_codes<kFp8, true>(v[p], f, ss, r)
+                                 : block_codes<kFp8, false>(v[p], 1.0f, ss, r);
     }
 }
 
@@ -342,9 +394,26 @@ hipError_t launch_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H
     if (tasks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)tasks), block(kThreads);
     if (D == 64)
-        quantize_qk_kernel<64><<<grid, block, 0, stream>>>(x, L, H, ld, nblk, q, s);
+        quantize_qk_kernel<64, false><<<grid, block, 0, stream>>>(x, L, H, ld, nblk, q, s);
     else if (D == 128)
-        quantize_qk_kernel<128><<<grid, block, 0, stream>>>(x, L, H, ld, nblk, q, s);
+        quantize_qk_kernel<128, false><<<grid, block, 0, stream>>>(x, L, H, ld, nblk, q, s);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_v_fp8(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                                 uint8_t *q, float *s, hipStream_t stream) {
+    const int64_t nblk = (L + kBlock - 1) / kBlock;
+    const int64_t tasks = B * H * nblk;
+    if (tasks <= 0) return hipSuccess;
+    if (tasks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tasks), block(kThreads);
+    int8_t *qb = reinterpret_cast<int8_t *>(q);
+    if (D == 64)
+        quantize_qk_kernel<64, true><<<grid, block, 0, stream>>>(x, L, H, ld, nblk, qb, s);
+    else if (D == 128)
+        quantize_qk_kernel<128, true><<<grid, block, 0, stream>>>(x, L, H, ld, nblk, qb, s);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

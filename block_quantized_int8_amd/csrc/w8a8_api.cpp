@@ -342,6 +342,20 @@ int w8a8_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_
     return hip_status(w8a8::launch_quantize_qk(static_cast<const uint16_t *>(x_bf16), B, L, H, D, ld, q, s, stream));
 }
 
+int w8a8_quantize_v_fp8(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, uint8_t *q,
+                        float *s, hipStream_t stream) {
+    if (!x_bf16 || !q || !s || B <= 0 || L <= 0 || H <= 0 || D <= 0) return W8A8_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return W8A8_ERR_UNSUPPORTED;
+    if (H > INT32_MAX / D) return W8A8_ERR_UNSUPPORTED;
+    if (ld < H * D) return W8A8_ERR_INVALID_ARG;
+    if (ld % 8 || !aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(s, 4)) return W8A8_ERR_UNSUPPORTED;
+    const int64_t nblk = (L + W8A8_BLOCK - 1) / W8A8_BLOCK;
+    if (B > INT32_MAX / H || B * H > INT32_MAX / nblk) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(q) || !is_device_ptr(s)) return W8A8_ERR_INVALID_ARG;
+    return hip_status(
+        w8a8::launch_quantize_v_fp8(static_cast<const uint16_t *>(x_bf16), B, L, H, D, ld, q, s, stream));
+}
+
 static int rope_args(const void *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, const float *cos_t,
                      const float *sin_t) {
     if (!x || !cos_t || !sin_t || B <= 0 || L <= 0 || H <= 0 || D <= 0) return W8A8_ERR_INVALID_ARG;

@@ -40,6 +40,8 @@ hipError_t launch_gemm_i8_blockscale_residual(const int8_t *qx, const float *sx,
                                               uint16_t *y, hipStream_t stream);
 hipError_t launch_gated_residual(const uint16_t *h, const uint16_t *o, const uint16_t *gate, int64_t B, int64_t L,
                                  int64_t N, uint16_t *y, hipStream_t stream);
+hipError_t launch_quantize_v_fp8(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
+                                 uint8_t *q, float *s, hipStream_t stream);
 hipError_t launch_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,
                               int8_t *q, float *s, hipStream_t stream);
 hipError_t launch_rope_quantize_qk(const uint16_t *x, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld,

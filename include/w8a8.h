@@ -354,6 +354,19 @@ int w8a8_quantize_qk(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_
                      float *s, hipStream_t stream);
 
 /*
+ * Attention V in FP8 beside the INT8 Q/K (same paragraph: the value
+ * aggregation takes FP8 values), in the same blocks and layout as
+ * w8a8_quantize_qk: per (b, h) and block of 128 tokens x D,
+ * s = fl32(max |x| / 448) and code = E4M3(fl32(x / s)), the OCP FP8 format
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest finite 448,
+ * no infinities), nearest with ties to the even code; an all-zero block has
+ * s = 0 and codes 0.  q uint8 [B, H, L, D] (head-major, E4M3 bit patterns),
+ * s fp32 [B, H, ceil(L/128)].  Arguments and errors as for w8a8_quantize_qk.
+ */
+int w8a8_quantize_v_fp8(const void *x_bf16, int64_t B, int64_t L, int64_t H, int64_t D, int64_t ld, uint8_t *q,
+                        float *s, hipStream_t stream);
+
+/*
  * Split-halves rotary position embedding of attention Q or K (TurboT2VA
  * paper, architecture-aware inference stack, fused-kernels paragraph, which
  * lists split rotary embeddings among the fused patterns), which precedes

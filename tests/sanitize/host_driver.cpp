@@ -48,6 +48,8 @@ hipError_t launch_modulate_quantize(const uint16_t *, const float *, bool, int64
                                     const uint16_t *, const uint16_t *, int8_t *, float *, hipStream_t) {
     reached("modulate_quantize");
 }
+hipError_t launch_quantize_v_fp8(const uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t, uint8_t *, float *,
+                                 hipStream_t) { reached("quantize_v_fp8"); }
 hipError_t launch_ln_rows(const uint16_t *, int64_t, int64_t, double, float *, hipStream_t) { reached("ln_rows"); }
 }  // namespace w8a8
 
@@ -117,6 +119,14 @@ int main() {
     CHECK(w8a8_quantize_qk(p, 1, 256, 2, 96, 192, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_quantize_qk(p, 1, 256, 2, 128, 255, q8, f, nullptr) == W8A8_ERR_INVALID_ARG);
     CHECK(w8a8_quantize_qk(p, 1LL << 40, 256, 1LL << 20, 128, 1LL << 27, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
+    // FP8 V: as for Q/K
+    CHECK(w8a8_quantize_v_fp8(p, 1, 256, 2, 96, 192, reinterpret_cast<uint8_t *>(q8), f, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_quantize_v_fp8(p, 1, 256, 2, 128, 255, reinterpret_cast<uint8_t *>(q8), f, nullptr) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_quantize_v_fp8(p, 1, 256, 2, 128, 256, nullptr, f, nullptr) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_quantize_v_fp8(p, 1, 256, 2, 128, 256, reinterpret_cast<uint8_t *>(q8), f, nullptr) ==
+          W8A8_ERR_INVALID_ARG);                                                                   // host memory
     // rotary embedding: head dimension, stride, table alignment, sizes, missing outputs
     CHECK(w8a8_rope_bf16(p, 1, 256, 2, 96, 192, f, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_rope_bf16(p, 1, 256, 2, 128, 255, f, f, p, nullptr) == W8A8_ERR_INVALID_ARG);
