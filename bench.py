@@ -20,7 +20,7 @@ three; the MLP producer fused with the quantization (exact GELU + 128x128
 block quantize of the MLP's hidden activation, 32768 x 16384) against GELU
 and quantize run one after the other; the INT8 quantization of a video
 self-attention's Q and K (28672 tokens x 32 heads x 128, read from a fused
-Q/K/V output) into the head-major layout, and the same with the split-halves
+Q/K/V output) into the head-major layout (and V into FP8), and the same with the split-halves
 rotary embedding fused in front of it against rotation then quantization;
 the guard's bf16 fallback; and a
 two-stream step (an INT8 linear and a guarded-to-bf16 linear launched on
@@ -543,6 +543,24 @@ def main():
     log(f"Q/K INT8 [{AL}, {AH}x{AD}] from a fused QKV output: {qk_us:.1f} us per tensor "
         f"({QK_BYTES / qk_us / 1e3:.0f} GB/s)")
 
+    # V in FP8 from the same fused output (its third column slice, here a copy of K's values)
+    qkv[:, 2 * AH * AD:] = qkv[:, AH * AD:2 * AH * AD]
+    vq = torch.empty((AH, AL, AD), dtype=torch.uint8, device=dev)
+    w8a8.quantize_v_fp8(qkv[:, 2 * AH * AD:], AH, vq, sq)   # untimed first launch
+    torch.cuda.synchronize()
+    v_t = []
+    for i in range(args.steps):
+        flush.amax()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        w8a8.quantize_v_fp8(qkv[:, 2 * AH * AD:], AH, vq, sq)
+        b.record()
+        v_t.append((a, b))
+    torch.cuda.synchronize()
+    v_us = sum(a.elapsed_time(b) for a, b in v_t) / len(v_t) * 1e3
+    del vq
+    log(f"V FP8 [{AL}, {AH}x{AD}]: {v_us:.1f} us ({QK_BYTES / v_us / 1e3:.0f} GB/s)")
+
     # rotary embedding + Q/K INT8: fused vs rotation to bf16 then quantization
     cs, sn = rope_tables_dev(dev)
     yrot = torch.empty((AL, AH * AD), dtype=torch.bfloat16, device=dev)
@@ -810,6 +828,12 @@ def main():
                                    "bf16 tensors; V stands in for the attention output (not part of a step)",
                            "fused_us": round(blk_us["fused"], 1), "unfused_us": round(blk_us["unfused"], 1),
                            "speedup": round(blk_us["unfused"] / blk_us["fused"], 3)},
+        "v_fp8_quantize": {"note": "attention V in FP8 E4M3 (s = max-abs/448 per 128 tokens x head) from the "
+                                   "third column slice of the fused Q/K/V output -> head-major codes (not part "
+                                   "of a step)",
+                           "us": round(v_us, 2), "gbs": round(QK_BYTES / v_us / 1e3, 1),
+                           "frac_of_hbm": round(QK_BYTES / v_us / 1e3 / PEAK_HBM_GBS, 4),
+                           "algorithmic_bytes": QK_BYTES},
         "rope_qk_ab": {"note": "split-halves rotary embedding fused into the INT8 Q/K quantizer vs rotation "
                                "to bf16 then quantization, per Q or K tensor of the video self-attention "
                                "(not part of a step); tables fp32 [tokens, head_dim/2]",
