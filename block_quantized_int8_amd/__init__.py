@@ -51,6 +51,9 @@ __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "rout
            "W8A8Error", "lib",
            "quantize_rows", "gemm_postscale", "linear_postscale", "postscale_workspace_bytes",
            "POSTSCALE_MAX_K", "gelu_bf16", "gelu_quantize_act", "quantize_qk",
+           "rmsnorm_modulate_bf16", "rmsnorm_modulate_quantize_act", "layernorm_modulate_bf16",
+           "layernorm_modulate_quantize_act", "rope_bf16", "rope_quantize_qk", "quantize_v_fp8",
+           "gated_residual", "gemm_blockscale_gated_residual",
            "PATH_INT8", "PATH_BF16", "DTYPE_BF16", "DTYPE_FP16", "DTYPE_FP32", "BLOCK", "EXPORTS"]
 
 _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32: DTYPE_FP32}

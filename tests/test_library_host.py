@@ -38,6 +38,16 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_package_exports_every_wrapper():
+    # every public function and class of the binding is in __all__, and
+    # every name in __all__ exists
+    import block_quantized_int8_amd as m
+    assert all(hasattr(m, n) for n in m.__all__)
+    public = [n for n, v in vars(m).items() if not n.startswith("_") and callable(v)
+              and getattr(v, "__module__", "") == m.__name__]
+    assert sorted(n for n in public if n not in m.__all__) == []
+
+
 def test_route_golden(L):
     g = load_golden("route_cases.json")
     for dt, M, K, N, hq, want, note in g["cases"]:
