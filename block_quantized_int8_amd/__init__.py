@@ -43,7 +43,7 @@ import ctypes
 
 import torch
 
-from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP16, DTYPE_FP32, EXPORTS, PATH_BF16, PATH_INT8,
+from ._lib import (BLOCK, BLOCK_MAX_K, DTYPE_BF16, DTYPE_FP16, DTYPE_FP32, EXPORTS, PATH_BF16, PATH_INT8,
                    POSTSCALE_MAX_K, W8A8Error, check, lib)
 
 __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "route",
@@ -558,7 +558,7 @@ class W8A8Linear(torch.nn.Module):
         if y.shape[-1] != K:
             raise ValueError(f"last dimension of y must be {K}")
         M = y.numel() // K
-        fused = (self.scaling == "block" and self.qweight is not None and M > 0
+        fused = (self.scaling == "block" and self.qweight is not None and M > 0 and K <= BLOCK_MAX_K
                  and route(torch.bfloat16, M, K, N, True) == PATH_INT8 and y.data_ptr() % 16 == 0)
         if not fused:
             return self.forward(gelu_bf16(y))
@@ -590,7 +590,7 @@ class W8A8Linear(torch.nn.Module):
         if Kx != K:
             raise ValueError(f"last dimension of x must be {K}")
         M = B * L
-        fused = (self.scaling == "block" and self.qweight is not None
+        fused = (self.scaling == "block" and self.qweight is not None and K <= BLOCK_MAX_K
                  and route(torch.bfloat16, M, K, N, True) == PATH_INT8 and x3.data_ptr() % 16 == 0
                  and scale.data_ptr() % 16 == 0 and shift.data_ptr() % 16 == 0)
         if not fused:
