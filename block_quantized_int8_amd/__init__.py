@@ -515,6 +515,10 @@ class W8A8Linear(torch.nn.Module):
     here: per 128x128 block (``scaling="block"``, the default) or per output
     channel (``scaling="postscale"``).  ``forward`` quantizes the activations
     on every call (or falls back) and returns bf16.
+
+    The quantized activations go to a workspace cached on the layer and
+    reused by every call, so calls of one layer object on several streams
+    must not overlap: order them, or give each stream its own layer.
     """
 
     def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, scaling: str = "block"):
