@@ -333,8 +333,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the layer shards by rows with no communication; see the design notes). "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the layer would shard by rows of X, with no communication). "
               "Run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
 

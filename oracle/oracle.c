@@ -44,8 +44,8 @@
  *       and Gimpel, "Gaussian Error Linear Units"), rounded once to bf16;
  *       the fused producer's result is that bf16 matrix block-quantized.
  *
- * Readings taken where the pages are silent (each also listed with the
- * design notes): correctly rounded fp32 division x/s; rint half-to-even;
+ * Readings taken where the pages are silent: correctly rounded fp32
+ * division x/s; rint half-to-even;
  * clamp to [-127, 127]; an all-zero block has s = 0 and q = 0 (no epsilon
  * floor); fp32 scales stored row-major [rows/128, K/128]; exact int32 sum per
  * 128-deep K-block, fp64 accumulation across K-blocks, one rounding fp64 ->
