@@ -70,17 +70,20 @@ def test_linear_step_replays(M, K, N, int8):
 
 
 def test_producer_and_qk_replay():
-    # fused GELU + quantize and INT8 Q/K in one graph
+    # fused GELU + quantize, INT8 Q/K and FP8 V in one graph
     M, K, H, D = 256, 512, 4, 128
     yh = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
     q = torch.empty((M, K), dtype=torch.int8, device="cuda")
     s = torch.empty((M // 128, K // 128), dtype=torch.float32, device="cuda")
     kq = torch.empty((H, M, D), dtype=torch.int8, device="cuda")
     ks = torch.empty((H, M // 128), dtype=torch.float32, device="cuda")
+    vq = torch.empty((1, H, M, D), dtype=torch.uint8, device="cuda")
+    vs = torch.empty((1, H, M // 128), dtype=torch.float32, device="cuda")
 
     def work():
         w8a8.gelu_quantize_act(yh, q, s)
         w8a8.quantize_qk(yh, H, kq, ks)
+        w8a8.quantize_v_fp8(yh, H, vq, vs)
 
     yh.copy_(to_dev_bf16(random_bf16(40, (M, K))))
     g = capture(work)
@@ -93,6 +96,8 @@ def test_producer_and_qk_replay():
         assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
         kq_o, ks_o = oracle.quantize_qk(host, 1, M, H, D, K)
         assert np.array_equal(kq.cpu().numpy(), kq_o[0]) and np.array_equal(ks.cpu().numpy(), ks_o[0])
+        vq_o, vs_o = oracle.quantize_v_fp8(host, 1, M, H, D, K)
+        assert np.array_equal(vq.cpu().numpy(), vq_o) and np.array_equal(vs.cpu().numpy(), vs_o)
 
 
 def test_block_slice_replay():
