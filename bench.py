@@ -58,6 +58,8 @@ GEMM_BYTES = M * K + N * K + (M // 128 + N // 128) * (K // 128) * 4 + M * N * 2
 GEMM_OPS = 2 * M * N * K
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_i8_attnproj.json")
 GEMM_SOURCE = os.path.join(ROOT, "block_quantized_int8_amd", "csrc", "gemm_i8_blockscale.hip")
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_block_attnproj.json")
+QUANT_SOURCE = os.path.join(ROOT, "block_quantized_int8_amd", "csrc", "quantize_block.hip")
 CPU_SAMPLE_BLOCKS = 256     # 128-row blocks of X the oracle processes (all 32768 rows)
 # MLP hidden activation (input of the fused GELU + quantize producer)
 HM, HK = 32768, 16384
@@ -96,15 +98,16 @@ def code_sha(path):
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or
-    None when absent or taken on different kernel code."""
+def load_traffic(path=TRAFFIC_FILE, source=GEMM_SOURCE):
+    """HBM bytes per launch of a kernel (the GEMM by default) from committed
+    rocprofv3 counter runs, or None when absent or taken on different
+    kernel code."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("code_sha") != code_sha(GEMM_SOURCE):
+    if t.get("code_sha") != code_sha(source):
         return None
     return t.get("bytes_per_launch")
 
@@ -786,6 +789,7 @@ def main():
         "roofline_quantize": {"bound": "hbm", "kernel": "quantize_block",
                               "achieved": round(quant_gbs, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
+                              "traffic": load_traffic(QUANT_TRAFFIC_FILE, QUANT_SOURCE),
                               "algorithmic_bytes": QUANT_BYTES},
         "cpu_baseline": cpu,
         "postscale_ab": {"note": "post-scale form on the same shape (not the headline path)",
