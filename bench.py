@@ -327,7 +327,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "rope", "rms",
+    ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "v", "rope", "rms",
                                        "ln", "residual"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -380,6 +380,16 @@ def main():
             w8a8.quantize_qk(qkv[:, :AH * AD], AH, qq, sq)
         torch.cuda.synchronize()
         log(f"--only qk: {args.steps} launches done")
+        return
+
+    if args.only == "v":
+        qkv, _, sq = qk_buffers(dev)
+        qkv[:, 2 * AH * AD:] = qkv[:, AH * AD:2 * AH * AD]
+        vq = torch.empty((AH, AL, AD), dtype=torch.uint8, device=dev)
+        for _ in range(args.steps):
+            w8a8.quantize_v_fp8(qkv[:, 2 * AH * AD:], AH, vq, sq)
+        torch.cuda.synchronize()
+        log(f"--only v: {args.steps} launches done")
         return
 
     if args.only == "rope":
