@@ -34,37 +34,43 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
                                "or python oracle/build.py")
-        L = ctypes.CDLL(_LIB_PATH)
-        L.oracle_quantize_block.argtypes = [_P, _I64, _I64, _P, _P]
-        L.oracle_kblock_partials.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P]
-        L.oracle_linear_int8_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
-        L.oracle_linear_bf16_rows.argtypes = [_P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
-        L.oracle_route.argtypes = [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int]
-        L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
-        L.oracle_f64_to_bf16.restype = ctypes.c_uint16
-        L.oracle_fp16_to_f64.argtypes = [ctypes.c_uint16]
-        L.oracle_fp16_to_f64.restype = ctypes.c_double
-        L.oracle_gelu_bf16.argtypes = [_P, _I64, _P]
-        L.oracle_quantize_rows.argtypes = [_P, _I64, _I64, _P, _P]
-        L.oracle_linear_postscale_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
-        L.oracle_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
-        L.oracle_rmsnorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
-        L.oracle_rope.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
-        L.oracle_gated_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
-        L.oracle_layernorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
-        L.oracle_quantize_v_fp8.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
-        L.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
-        L.oracle_f32_to_e4m3.restype = ctypes.c_uint8
-        L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
-        L.oracle_e4m3_to_f64.restype = ctypes.c_double
-        for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
-                  "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
-                  "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
-                  "oracle_quantize_qk", "oracle_rmsnorm_modulate", "oracle_rope",
-                  "oracle_gated_residual", "oracle_layernorm_modulate", "oracle_quantize_v_fp8"):
-            getattr(L, f).restype = ctypes.c_int
-        _lib = L
+        _lib = load(_LIB_PATH)
     return _lib
+
+
+def load(path):
+    """ctypes handle of an oracle build at ``path`` with every signature set
+    (the mutation tests load deliberately broken copies this way)."""
+    L = ctypes.CDLL(path)
+    L.oracle_quantize_block.argtypes = [_P, _I64, _I64, _P, _P]
+    L.oracle_kblock_partials.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P]
+    L.oracle_linear_int8_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+    L.oracle_linear_bf16_rows.argtypes = [_P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
+    L.oracle_route.argtypes = [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int]
+    L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+    L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    L.oracle_fp16_to_f64.argtypes = [ctypes.c_uint16]
+    L.oracle_fp16_to_f64.restype = ctypes.c_double
+    L.oracle_gelu_bf16.argtypes = [_P, _I64, _P]
+    L.oracle_quantize_rows.argtypes = [_P, _I64, _I64, _P, _P]
+    L.oracle_linear_postscale_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
+    L.oracle_quantize_qk.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
+    L.oracle_rmsnorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
+    L.oracle_rope.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
+    L.oracle_gated_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
+    L.oracle_layernorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P]
+    L.oracle_quantize_v_fp8.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
+    L.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    L.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    L.oracle_e4m3_to_f64.restype = ctypes.c_double
+    for f in ("oracle_quantize_block", "oracle_kblock_partials", "oracle_linear_int8_rows",
+              "oracle_linear_bf16_rows", "oracle_route", "oracle_gelu_bf16",
+              "oracle_num_threads", "oracle_quantize_rows", "oracle_linear_postscale_rows",
+              "oracle_quantize_qk", "oracle_rmsnorm_modulate", "oracle_rope",
+              "oracle_gated_residual", "oracle_layernorm_modulate", "oracle_quantize_v_fp8"):
+        getattr(L, f).restype = ctypes.c_int
+    return L
 
 
 def _ptr(a):

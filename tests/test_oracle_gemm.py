@@ -107,6 +107,31 @@ def test_error_bound_vs_exact_product(seed):
     assert np.linalg.norm(y64 - exact) / np.linalg.norm(exact) < 0.05
 
 
+def test_output_rounded_once_from_the_full_sum():
+    """Hand-worked: the K-block sum is rounded to bf16 once, not through fp32.
+
+    K-block 0 has unit scales and partial 127*2 + 3*1 = 257; K-block 1 has
+    combined scale 2^-10 * 2^-10 and partial 1, so Y = 257 + 2^-20 exactly.
+    bf16 spacing in [256, 512) is 2: 257 is the midpoint of 256 (0x4380) and
+    258 (0x4381), and Y lies just above it, so Y -> 258.  Through fp32 (ulp
+    2^-15 there) Y would first become 257, a tie that goes to the even 256.
+    Column 1 has the same partials with the weight code of K-block 1 negated:
+    257 - 2^-20 -> 256 either way.
+    """
+    qx = np.zeros((128, 256), np.int8)
+    qw = np.zeros((128, 256), np.int8)
+    qx[0, 0], qw[0, 0] = 127, 2
+    qx[0, 1], qw[0, 1] = 3, 1
+    qx[0, 128], qw[0, 128] = 1, 1
+    qw[1, 0], qw[1, 1], qw[1, 128] = 2, 1, -1
+    sx = np.array([[1.0, 2.0 ** -10]], np.float32)
+    sw = np.array([[1.0, 2.0 ** -10]], np.float32)
+    y, y64 = oracle.linear_int8(qx, sx, qw, sw, rows=[0], want_f64=True)
+    assert y64[0, 0] == 257 + 2.0 ** -20 and y64[0, 1] == 257 - 2.0 ** -20
+    assert y[0, 0] == 0x4381 and y[0, 1] == 0x4380
+    assert np.all(y[0, 2:] == 0)
+
+
 def test_kblock_separability():
     # Y (fp64, before rounding) is the sum over K-blocks of the contributions
     # of each K-block alone: quantizing a matrix with all other K-blocks
