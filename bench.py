@@ -7,26 +7,32 @@ On this shape the guard takes the INT8 path, so a step is the dynamic
 128x128 activation quantization followed by the INT8 GEMM with per-K-block
 dequantization and bf16 output.  The weight is quantized once, before
 timing (static weights).  Inputs are resident in HBM when timing starts.
+A fixed settle phase (SETTLE_S seconds of steps) runs ahead of the --warmup
+steps: from a cold start the GPU clock dips for its first dozen or so
+GEMM launches, and a continuously running layer never sees that transient.
 
 Printed: one JSON line with the whole-step throughput (value, in TOPS of
 2*M*N*K per step), the per-kernel figures measured with HIP events on the
 stream the kernels run on, the roofline of the dominant kernel (the GEMM,
-bound by the INT8 MFMA peak) and the CPU oracle timed on a bounded sample of
+bound by the INT8 MFMA peak), the GPU clock sampled during a run of
+back-to-back GEMM launches, and the CPU oracle timed on a bounded sample of
 the same workload on this host.
 
-Also measured (reported beside the headline, not part of a step): the
-post-scale form on the same shape; Q, K, V as one concatenated linear vs
-three; the MLP producer fused with the quantization (exact GELU + 128x128
-block quantize of the MLP's hidden activation, 32768 x 16384) against GELU
-and quantize run one after the other; the INT8 quantization of a video
-self-attention's Q and K (28672 tokens x 32 heads x 128, read from a fused
-Q/K/V output) into the head-major layout (and V into FP8), and the same with the split-halves
-rotary embedding fused in front of it against rotation then quantization;
-the guard's bf16 fallback; and a
-two-stream step (an INT8 linear and a guarded-to-bf16 linear launched on
-two streams at once).
+The other workloads of the scope table are measured beside it (not part of a
+step): the 256^3 single linear, the 4096^3 square linear, the MLP pair's up
+(32768 x 16384 x 4096) and down (32768 x 4096 x 16384) projections and the
+two-stream step's INT8 stream (65536 x 4096 x 4096): each with its GEMM
+(TOPS, fraction of peak), its activation quantization (GB/s, fraction of
+HBM) and the oracle timed on one 128-row block of it; the guard's bf16
+fallback (M = 4000 and 1000 x 2048 x 2048) and the two-stream step itself;
+the post-scale form; the producers fused with the quantization (exact
+GELU, modulated RMSNorm and LayerNorm); Q, K, V as one concatenated linear
+vs three; and the INT8 quantization of a video self-attention's Q and K.
+--extras adds the measurements of patterns beyond that table: V in FP8,
+the rotary embedding fused into the Q/K quantizer, the gated residual update
+in the GEMM epilogue and one transformer block's W8A8 work.
 
-Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|rope|rms|ln|residual
+Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|v|rope|rms|ln|residual|mlp_up|mlp_down
 launches just that work for --steps iterations (no oracle);
 --copy-calibration runs a plain 1 GiB device copy used to scale the HBM byte
 counters.
@@ -322,16 +328,237 @@ def producer_buffers(w8a8, dev):
     return yh, xh, qh, sh
 
 
+SETTLE_S = 1.0          # seconds of steps ahead of the --warmup steps (clock settle)
+CLOCK_LOOP_S = 0.3      # seconds of back-to-back GEMM launches while the clock is sampled
+ORACLE_ROWS = 128       # rows (one 128-row block) of each extra workload the oracle is timed on
+
+
+class ClockSampler:
+    """Samples the GPU's gfx clock (MHz, the mean over the chip's XCDs) from
+    the SMI library's GPU metrics every ~2 ms in a background thread."""
+
+    def __init__(self):
+        self.samples, self.error, self._h = [], None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception as exc:  # no SMI access on this host: reported, not fatal
+            self.error = f"{type(exc).__name__}: {exc}"
+            self._h = None
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if xs:
+            return sum(xs) / len(xs)
+        c = m.get("current_gfxclk")
+        return float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None
+
+    def run(self, fn):
+        """Calls fn() while sampling; returns fn's result."""
+        import threading
+        if self._h is None:
+            return fn()
+        stop = threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    v = self._read()
+                    if v:
+                        self.samples.append(v)
+                except Exception as exc:
+                    self.error = f"{type(exc).__name__}: {exc}"
+                time.sleep(0.002)
+
+        th = threading.Thread(target=loop, daemon=True)
+        th.start()
+        try:
+            return fn()
+        finally:
+            stop.set()
+            th.join()
+
+
+def event_times(fns, reps, flush=None):
+    """Median and mean us of each callable over `reps` rounds (one HIP event
+    pair around each launch on the current stream), rounds interleaved;
+    `flush` (if given) runs untimed before every launch."""
+    import statistics
+    import torch
+    res = {k: [] for k in fns}
+    for _ in range(reps):
+        for k, fn in fns.items():
+            if flush is not None:
+                flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            res[k].append((a, b))
+    torch.cuda.synchronize()
+    out = {}
+    for k, v in res.items():
+        us = [a.elapsed_time(b) * 1e3 for a, b in v]
+        out[k] = {"median": statistics.median(us), "mean": sum(us) / len(us)}
+    return out
+
+
+def gpu_normal(gen, shape, scale=1.0, outlier_frac=0.0, outlier_factor=1.0, dev="cuda"):
+    """Seeded N(0, scale^2) bf16 tensor made on the GPU (fp32 draw, optional
+    outlier channels scaled in fp32, one conversion to bf16), for the workloads
+    that are timed only."""
+    import torch
+    a = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    if scale != 1.0:
+        a *= scale
+    if outlier_frac:
+        k = shape[-1]
+        ch = torch.randperm(k, generator=gen, device=dev)[:int(round(outlier_frac * k))]
+        a[:, ch] *= outlier_factor
+    return a.to(torch.bfloat16)
+
+
+def oracle_rows_seconds(x_rows_bf16, w_bf16):
+    """Oracle time (s) for the quantization of a block of activation rows and
+    their full output rows; the static weight quantization is done first and
+    not counted."""
+    import numpy as np
+    import torch
+    import oracle
+    xs = np.ascontiguousarray(x_rows_bf16.view(torch.int16).cpu().numpy().view(np.uint16))
+    ws = np.ascontiguousarray(w_bf16.view(torch.int16).cpu().numpy().view(np.uint16))
+    qw, sw = oracle.quantize_block(ws)
+    t0 = time.perf_counter()
+    qx, sx = oracle.quantize_block(xs)
+    oracle.linear_int8(qx, sx, qw, sw)
+    return time.perf_counter() - t0
+
+
+def measure_config(w8a8, name, x, w, flush, reps, with_oracle=True, note=""):
+    """Activation quantization and INT8 block GEMM of one workload: us, TOPS,
+    fractions of the peaks, and the oracle on one 128-row block."""
+    import torch
+    M, K = x.shape
+    N = w.shape[0]
+    qw, sw = w8a8.quantize_weight(w)
+    qx, sx = w8a8.quantize_act(x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    w8a8.gemm_blockscale(qx, sx, qw, sw, out=y)
+    torch.cuda.synchronize()
+    g = event_times({"gemm": lambda: w8a8.gemm_blockscale(qx, sx, qw, sw, out=y)}, reps)["gemm"]
+    q = event_times({"q": lambda: w8a8.quantize_act(x, qx, sx)}, reps, flush=flush)["q"]
+    ops = 2 * M * N * K
+    qbytes = M * K * 3 + (M // 128) * (K // 128) * 4
+    tops = ops / (g["median"] * 1e-6) / 1e12
+    gbs = qbytes / (q["median"] * 1e-6) / 1e9
+    out = {"shape": [M, N, K], "gemm_us": round(g["median"], 2), "gemm_tops": round(tops, 1),
+           "gemm_frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
+           "quantize_us": round(q["median"], 2), "quantize_gbs": round(gbs, 1),
+           "quantize_frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4), "quantize_bytes": qbytes, "gemm_ops": ops}
+    if note:
+        out["note"] = note
+    if with_oracle:
+        import oracle
+        rows = min(ORACLE_ROWS, M)
+        secs = oracle_rows_seconds(x[:rows], w)
+        out["oracle"] = {"rows": rows, "seconds": round(secs, 3), "cores": oracle.num_threads(),
+                         "full_seconds_extrapolated": round(secs * M / rows, 2),
+                         "tops": round(2 * rows * N * K / secs / 1e12, 4)}
+    log(f"{name} {M}x{N}x{K}: gemm {g['median']:.1f} us = {tops:.0f} TOPS ({tops / PEAK_INT8_TOPS:.1%}); "
+        f"quantize {q['median']:.1f} us = {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%})"
+        + (f"; oracle {out['oracle']['seconds']} s / {out['oracle']['rows']} rows" if with_oracle else ""))
+    del qx, sx, qw, sw, y
+    return out
+
+
+def extras(w8a8, dev, args, x, y, qx, sx, qw, sw, flush):
+    """Patterns beyond the scope table: V in FP8, the rotary embedding fused
+    into the Q/K quantizer, the gated residual update in the GEMM epilogue and
+    one transformer block's W8A8 work."""
+    import torch
+    res = {}
+    hres, gres, yres = residual_buffers(dev)
+    runs = {"fused": lambda: w8a8.gemm_blockscale_gated_residual(qx, sx, qw, sw, hres, gres, out=yres),
+            "gemm": lambda: w8a8.gemm_blockscale(qx, sx, qw, sw, out=y),
+            "update": lambda: w8a8.gated_residual(hres, y, gres, out=yres)}
+    for fn in runs.values():
+        fn()
+    torch.cuda.synchronize()
+    t = event_times(runs, args.steps, flush=flush)
+    r = {k: v["median"] for k, v in t.items()}
+    del hres, gres, yres
+    res["gated_residual_ab"] = {
+        "note": "gated residual update h + gate * o of the attention projection's output (4 batch entries of "
+                "8192 tokens) in the block GEMM's epilogue vs the GEMM then the update kernel",
+        "shape": [M, N, K], "batch_entries": RES_B, "fused_us": round(r["fused"], 2),
+        "unfused_gemm_us": round(r["gemm"], 2), "unfused_update_us": round(r["update"], 2),
+        "update_gbs": round(RES_UPDATE_BYTES / r["update"] / 1e3, 1),
+        "speedup": round((r["gemm"] + r["update"]) / r["fused"], 3)}
+    log(f"gated residual: fused {r['fused']:.1f} us vs GEMM {r['gemm']:.1f} + update {r['update']:.1f} us")
+
+    qkv, qq, sq = qk_buffers(dev)
+    qkv[:, 2 * AH * AD:] = qkv[:, AH * AD:2 * AH * AD]
+    vq = torch.empty((AH, AL, AD), dtype=torch.uint8, device=dev)
+    w8a8.quantize_v_fp8(qkv[:, 2 * AH * AD:], AH, vq, sq)
+    torch.cuda.synchronize()
+    v_us = event_times({"v": lambda: w8a8.quantize_v_fp8(qkv[:, 2 * AH * AD:], AH, vq, sq)}, args.steps,
+                       flush=flush)["v"]["median"]
+    del vq
+    res["v_fp8_quantize"] = {"note": "attention V in FP8 E4M3 (s = max-abs/448 per 128 tokens x head) from the "
+                                     "third column slice of the fused Q/K/V output -> head-major codes",
+                             "us": round(v_us, 2), "gbs": round(QK_BYTES / v_us / 1e3, 1),
+                             "frac_of_hbm": round(QK_BYTES / v_us / 1e3 / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes": QK_BYTES}
+    log(f"V FP8: {v_us:.1f} us")
+
+    cs, sn = rope_tables_dev(dev)
+    yrot = torch.empty((AL, AH * AD), dtype=torch.bfloat16, device=dev)
+    rope_runs = {"fused": lambda: w8a8.rope_quantize_qk(qkv[:, :AH * AD], AH, cs, sn, qq, sq),
+                 "rotate": lambda: w8a8.rope_bf16(qkv[:, :AH * AD], AH, cs, sn, out=yrot),
+                 "quantize": lambda: w8a8.quantize_qk(yrot, AH, qq, sq)}
+    for fn in rope_runs.values():
+        fn()
+    torch.cuda.synchronize()
+    r = {k: v["median"] for k, v in event_times(rope_runs, args.steps, flush=flush).items()}
+    del qkv, qq, sq, yrot, cs, sn
+    res["rope_qk_ab"] = {"note": "split-halves rotary embedding fused into the INT8 Q/K quantizer vs rotation "
+                                 "to bf16 then quantization, per Q or K tensor; tables fp32 [tokens, head_dim/2]",
+                         "shape": {"tokens": AL, "heads": AH, "head_dim": AD, "row_stride": 3 * AH * AD,
+                                   "table_grid": list(ROPE_GRID)},
+                         "fused_us": round(r["fused"], 2),
+                         "fused_gbs_algorithmic": round(ROPE_QK_BYTES / r["fused"] / 1e3, 1),
+                         "algorithmic_bytes": ROPE_QK_BYTES, "unfused_rotate_us": round(r["rotate"], 2),
+                         "unfused_quantize_us": round(r["quantize"], 2),
+                         "speedup": round((r["rotate"] + r["quantize"]) / r["fused"], 3)}
+    log(f"RoPE + Q/K: fused {r['fused']:.1f} us vs {r['rotate']:.1f} + {r['quantize']:.1f} us")
+
+    blk = block_slice_ab(w8a8, dev, args.steps)
+    res["block_slice_ab"] = {"note": "one transformer block's W8A8 work, attention excluded (4 x 8192 tokens x "
+                                     "4096, 32 heads of 128, MLP 16384), every fusion in place vs the same steps "
+                                     "through bf16 tensors",
+                             "fused_us": round(blk["fused"], 1), "unfused_us": round(blk["unfused"], 1),
+                             "speedup": round(blk["unfused"] / blk["fused"], 3)}
+    log(f"block slice: fused {blk['fused']:.1f} us vs unfused {blk['unfused']:.1f} us")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "v", "rope", "rms",
-                                       "ln", "residual"],
+                                       "ln", "residual", "mlp_up", "mlp_down"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extras", action="store_true",
+                    help="also measure the patterns beyond the scope table (FP8 V, fused RoPE, gated residual, "
+                         "block slice)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -341,12 +568,14 @@ def main():
               "Run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
 
+    import numpy as np
     import torch
     ensure_built()
     import block_quantized_int8_amd as w8a8
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    t_start = time.perf_counter()
 
     if args.copy_calibration:
         n = 1 << 30
@@ -357,6 +586,23 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy calibration: {args.steps} copies of {n} bytes")
+        return
+
+    if args.only in ("mlp_up", "mlp_down"):
+        gen = torch.Generator(device=dev).manual_seed(3)
+        if args.only == "mlp_up":
+            xm, wm = gpu_normal(gen, (32768, 4096), dev=dev), gpu_normal(gen, (16384, 4096), 0.02, dev=dev)
+        else:
+            xm = w8a8.gelu_bf16(gpu_normal(gen, (32768, 16384), 1.28, dev=dev))
+            wm = gpu_normal(gen, (4096, 16384), 0.02, dev=dev)
+        qwm, swm = w8a8.quantize_weight(wm)
+        qxm, sxm = w8a8.quantize_act(xm)
+        ym = torch.empty((xm.shape[0], wm.shape[0]), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.steps):
+            w8a8.quantize_act(xm, qxm, sxm)
+            w8a8.gemm_blockscale(qxm, sxm, qwm, swm, out=ym)
+        torch.cuda.synchronize()
+        log(f"--only {args.only}: {args.steps} quantize + GEMM launches done")
         return
 
     t_gen = time.perf_counter()
@@ -440,12 +686,20 @@ def main():
         log(f"--only {args.only}: {args.steps} launches done")
         return
 
+    # ---- settle, warm-up, then the timed region: K whole steps
     assert step() == w8a8.PATH_INT8
+    torch.cuda.synchronize()
+    settle_steps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -456,7 +710,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"step: {ms_step * 1e3:.1f} us (events), wall {wall / args.steps * 1e6:.1f} us")
+    log(f"step: {ms_step * 1e3:.1f} us (events), wall {wall / args.steps * 1e6:.1f} us; "
+        f"settle {settle_steps} steps, warm-up {args.warmup}")
 
     # ---- per-kernel durations: events between the two launches of each
     # step, on the stream the kernels run on (torch's current stream)
@@ -470,24 +725,78 @@ def main():
     torch.cuda.synchronize()
     gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
 
+    # the GPU clock over back-to-back GEMM launches (sampled from the SMI
+    # metrics), and the GEMM's cycle efficiency at that clock
+    clk = ClockSampler()
+    n_clk = max(1, int(CLOCK_LOOP_S / (gemm_ms * 1e-3)))
+
+    def clock_loop():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n_clk):
+            w8a8.gemm_blockscale(qx, sx, qw, sw, out=y)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n_clk
+
+    clk_ms = clk.run(clock_loop)
+    if clk.samples:
+        mhz = sum(clk.samples) / len(clk.samples)
+        clk_tops = GEMM_OPS / (clk_ms * 1e-3) / 1e12
+        peak_at_clk = 256 * 8192 * mhz * 1e6 / 1e12
+        clock = {"source": "SMI GPU metrics: current gfx clock, mean over the XCDs, sampled every ~2 ms during "
+                           f"{n_clk} back-to-back GEMM launches",
+                 "mhz_mean": round(mhz, 1), "mhz_min": round(min(clk.samples), 1),
+                 "mhz_max": round(max(clk.samples), 1), "samples": len(clk.samples),
+                 "gemm_us_during": round(clk_ms * 1e3, 2),
+                 "gemm_frac_of_peak_at_this_clock": round(clk_tops / peak_at_clk, 4),
+                 "clock_frac_of_2400mhz": round(mhz / 2400.0, 4)}
+        log(f"clock during {n_clk} GEMMs: {mhz:.0f} MHz mean ({min(clk.samples):.0f}-{max(clk.samples):.0f}); "
+            f"GEMM {clk_ms * 1e3:.1f} us = {clk_tops / peak_at_clk:.1%} of the peak at that clock")
+    else:
+        clock = {"source": "SMI GPU metrics", "mhz_mean": None, "error": clk.error,
+                 "gemm_us_during": round(clk_ms * 1e3, 2)}
+        log(f"clock not sampled: {clk.error}")
+
     # quantize with the 256 MiB last-level cache flushed before each launch
     # by READING 1 GiB (a write-based flush would leave dirty lines whose
     # write-back competes with the timed kernel)
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    qt = []
-    for i in range(args.steps):
-        flush.amax()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        w8a8.quantize_act(x, qx, sx)
-        b.record()
-        qt.append((a, b))
-    torch.cuda.synchronize()
-    quant_ms = sum(a.elapsed_time(b) for a, b in qt) / args.steps
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush = flush_buf.amax
+    quant_ms = event_times({"q": lambda: w8a8.quantize_act(x, qx, sx)}, args.steps, flush=flush)["q"]["mean"] / 1e3
+
+    # ---- the other workloads of the scope table
+    reps = max(10, args.steps // 2)
+    configs = {}
+    gen = torch.Generator(device=dev).manual_seed(11)
+    from block_quantized_int8_amd.workloads import single_linear_256, square_4096
+    d1 = single_linear_256()
+    tb = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    configs["single_linear_256"] = measure_config(w8a8, "single linear", tb(d1["x"]), tb(d1["w"]), flush, reps,
+                                                  note="latency-bound; seeded workload bits")
+    d2 = square_4096()
+    x2, w2 = tb(d2["x"]), tb(d2["w"])
+    configs["square_4096"] = measure_config(w8a8, "square", x2, w2, flush, reps, note="seeded workload bits")
+    del d2, x2, w2
+    xu, wu = gpu_normal(gen, (32768, 4096), dev=dev), gpu_normal(gen, (16384, 4096), 0.02, dev=dev)
+    configs["mlp_up"] = measure_config(w8a8, "MLP up", xu, wu, flush, reps,
+                                       note="GPU-seeded N(0,1) activations, N(0, 0.02^2) weights")
+    del xu, wu
+    xd = w8a8.gelu_bf16(gpu_normal(gen, (32768, 16384), 1.28, dev=dev))
+    wd = gpu_normal(gen, (4096, 16384), 0.02, dev=dev)
+    configs["mlp_down"] = measure_config(w8a8, "MLP down", xd, wd, flush, reps,
+                                         note="input = exact GELU of GPU-seeded N(0, 1.28^2) (the up projection's "
+                                              "spread), 128 K-blocks per output")
+    del xd, wd
+    xa = gpu_normal(gen, (65536, 4096), outlier_frac=0.005, outlier_factor=30.0, dev=dev)
+    wa = gpu_normal(gen, (4096, 4096), 0.02, dev=dev)
+    configs["two_stream_a"] = measure_config(w8a8, "two-stream A", xa, wa, flush, reps,
+                                             note="GPU-seeded N(0,1), 0.5% of channels x30")
+    del xa, wa
+    torch.cuda.empty_cache()
 
     # shared-input projections: Q, K, V (3 x 4096 output channels) on X as
     # three guarded linears vs one group over the concatenated channels
-    import numpy as np
     from block_quantized_int8_amd.workloads import random_bf16
     wk = torch.from_numpy(random_bf16(51, (N, K), 0.02).view(np.int16)).to(dev).view(torch.bfloat16)
     wv = torch.from_numpy(random_bf16(52, (N, K), 0.02).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -513,91 +822,17 @@ def main():
     del group, projs, wk, wv
     log(f"QKV 32768x(3x4096)x4096: one group {qkv_group_us:.1f} us vs three linears {qkv_sep_us:.1f} us")
 
-    # gated residual update h + gate * o of the attention projection's output
-    # (4 batch entries x 8192 tokens): in the GEMM's epilogue vs the GEMM then
-    # the update kernel; each launch after a read flush
-    hres, gres, yres = residual_buffers(dev)
-    res_runs = {"fused": lambda: w8a8.gemm_blockscale_gated_residual(qx, sx, qw, sw, hres, gres, out=yres),
-                "gemm": lambda: w8a8.gemm_blockscale(qx, sx, qw, sw, out=y),
-                "update": lambda: w8a8.gated_residual(hres, y, gres, out=yres)}
-    for fn in res_runs.values():
-        fn()
-    torch.cuda.synchronize()
-    res_t = {k: [] for k in res_runs}
-    for i in range(args.steps):
-        for k, fn in res_runs.items():
-            flush.amax()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            res_t[k].append((a, b))
-    torch.cuda.synchronize()
-    res_us = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in res_t.items()}
-    del hres, gres, yres
-    log(f"gated residual: fused GEMM {res_us['fused']:.1f} us vs GEMM {res_us['gemm']:.1f} + update "
-        f"{res_us['update']:.1f} us")
-
     # INT8 attention Q and K from the fused Q/K/V output (row stride 3 * 4096)
     qkv, qq, sq = qk_buffers(dev)
     w8a8.quantize_qk(qkv[:, :AH * AD], AH, qq, sq)   # untimed first launch (code object load)
     torch.cuda.synchronize()
-    qk_t = []
-    for i in range(args.steps):
-        for col in (0, AH * AD):
-            flush.amax()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            w8a8.quantize_qk(qkv[:, col:col + AH * AD], AH, qq, sq)
-            b.record()
-            qk_t.append((a, b))
-    torch.cuda.synchronize()
-    qk_us = sum(a.elapsed_time(b) for a, b in qk_t) / len(qk_t) * 1e3
+    qk_t = event_times({"q": lambda: w8a8.quantize_qk(qkv[:, :AH * AD], AH, qq, sq),
+                        "k": lambda: w8a8.quantize_qk(qkv[:, AH * AD:2 * AH * AD], AH, qq, sq)},
+                       args.steps, flush=flush)
+    qk_us = (qk_t["q"]["mean"] + qk_t["k"]["mean"]) / 2
+    del qkv, qq, sq
     log(f"Q/K INT8 [{AL}, {AH}x{AD}] from a fused QKV output: {qk_us:.1f} us per tensor "
         f"({QK_BYTES / qk_us / 1e3:.0f} GB/s)")
-
-    # V in FP8 from the same fused output (its third column slice, here a copy of K's values)
-    qkv[:, 2 * AH * AD:] = qkv[:, AH * AD:2 * AH * AD]
-    vq = torch.empty((AH, AL, AD), dtype=torch.uint8, device=dev)
-    w8a8.quantize_v_fp8(qkv[:, 2 * AH * AD:], AH, vq, sq)   # untimed first launch
-    torch.cuda.synchronize()
-    v_t = []
-    for i in range(args.steps):
-        flush.amax()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        w8a8.quantize_v_fp8(qkv[:, 2 * AH * AD:], AH, vq, sq)
-        b.record()
-        v_t.append((a, b))
-    torch.cuda.synchronize()
-    v_us = sum(a.elapsed_time(b) for a, b in v_t) / len(v_t) * 1e3
-    del vq
-    log(f"V FP8 [{AL}, {AH}x{AD}]: {v_us:.1f} us ({QK_BYTES / v_us / 1e3:.0f} GB/s)")
-
-    # rotary embedding + Q/K INT8: fused vs rotation to bf16 then quantization
-    cs, sn = rope_tables_dev(dev)
-    yrot = torch.empty((AL, AH * AD), dtype=torch.bfloat16, device=dev)
-    w8a8.rope_quantize_qk(qkv[:, :AH * AD], AH, cs, sn, qq, sq)   # untimed first launches
-    w8a8.rope_bf16(qkv[:, :AH * AD], AH, cs, sn, out=yrot)
-    torch.cuda.synchronize()
-    rope_runs = {"fused": lambda v: w8a8.rope_quantize_qk(v, AH, cs, sn, qq, sq),
-                 "rotate": lambda v: w8a8.rope_bf16(v, AH, cs, sn, out=yrot),
-                 "quantize": lambda v: w8a8.quantize_qk(yrot, AH, qq, sq)}
-    rope_t = {k: [] for k in rope_runs}
-    for i in range(args.steps):
-        for col in (0, AH * AD):
-            for k, fn in rope_runs.items():
-                flush.amax()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                fn(qkv[:, col:col + AH * AD])
-                b.record()
-                rope_t[k].append((a, b))
-    torch.cuda.synchronize()
-    rope_us = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in rope_t.items()}
-    del qkv, qq, sq, yrot, cs, sn
-    log(f"RoPE + Q/K INT8 fused {rope_us['fused']:.1f} us per tensor vs rotate {rope_us['rotate']:.1f} + "
-        f"quantize {rope_us['quantize']:.1f} us")
 
     # the guard's bf16 fallback on the shapes that take it: M = 4000 (not a
     # multiple of 128) at 4096^2, and the two-stream workload's 1000 x 2048^2
@@ -609,13 +844,7 @@ def main():
         lf(xf)
         torch.cuda.synchronize()
         assert lf.last_path == w8a8.PATH_BF16
-        fa, fz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fa.record()
-        for _ in range(args.steps):
-            lf(xf)
-        fz.record()
-        torch.cuda.synchronize()
-        us = fa.elapsed_time(fz) / args.steps * 1e3
+        us = event_times({"f": lambda: lf(xf)}, args.steps)["f"]["median"]
         tf = 2 * fm * fn * fk / (us * 1e-6) / 1e12
         fb[name] = {"us": round(us, 2), "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         del xf, wf, lf
@@ -626,14 +855,13 @@ def main():
     # each alone
     from block_quantized_int8_amd.workloads import two_stream
     d5 = two_stream()
-    tensor = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    xa5, xb5 = tensor(d5["x_a"]), tensor(d5["x_b"])
-    la5, lb5 = w8a8.W8A8Linear(tensor(d5["w_a"])), w8a8.W8A8Linear(tensor(d5["w_b"]))
+    xa5, xb5 = tb(d5["x_a"]), tb(d5["x_b"])
+    la5, lb5 = w8a8.W8A8Linear(tb(d5["w_a"])), w8a8.W8A8Linear(tb(d5["w_b"]))
     del d5
     sa5, sb5 = torch.cuda.Stream(), torch.cuda.Stream()
     cur = torch.cuda.current_stream()
 
-    def two_stream(run_a, run_b):
+    def two_stream_run(run_a, run_b):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(cur)
         for _ in range(args.steps):
@@ -655,9 +883,9 @@ def main():
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / args.steps * 1e3
 
-    two_stream(True, True)  # untimed first launches
+    two_stream_run(True, True)  # untimed first launches
     assert la5.last_path == w8a8.PATH_INT8 and lb5.last_path == w8a8.PATH_BF16
-    ts_both, ts_a, ts_b = two_stream(True, True), two_stream(True, False), two_stream(False, True)
+    ts_both, ts_a, ts_b = two_stream_run(True, True), two_stream_run(True, False), two_stream_run(False, True)
     del xa5, xb5, la5, lb5
     log(f"two-stream step: both {ts_both:.1f} us; A alone {ts_a:.1f} us, B alone {ts_b:.1f} us")
 
@@ -667,60 +895,36 @@ def main():
     w8a8.gelu_quantize_act(yh, qh, sh)                # untimed first launches
     w8a8.gelu_bf16(yh, out=xh)
     torch.cuda.synchronize()
-    pt = {"fused": [], "gelu": [], "quantize": []}
-    for i in range(args.steps):
-        for key, fn in (("fused", lambda: w8a8.gelu_quantize_act(yh, qh, sh)),
-                        ("gelu", lambda: w8a8.gelu_bf16(yh, out=xh)),
-                        ("quantize", lambda: w8a8.quantize_act(xh, qh, sh))):
-            flush.amax()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            pt[key].append((a, b))
-    torch.cuda.synchronize()
-    prod_us = {k: sum(a.elapsed_time(b) for a, b in v) / args.steps * 1e3 for k, v in pt.items()}
+    pt = event_times({"fused": lambda: w8a8.gelu_quantize_act(yh, qh, sh),
+                      "gelu": lambda: w8a8.gelu_bf16(yh, out=xh),
+                      "quantize": lambda: w8a8.quantize_act(xh, qh, sh)}, args.steps, flush=flush)
+    prod_us = {k: v["mean"] for k, v in pt.items()}
     del yh, xh, qh, sh
     log(f"producer A/B (32768x16384): fused {prod_us['fused']:.1f} us "
         f"({PRODUCER_BYTES / prod_us['fused'] / 1e3:.0f} GB/s) vs gelu {prod_us['gelu']:.1f} + "
         f"quantize {prod_us['quantize']:.1f} us")
 
-    # producer A/B on a transformer block's input: modulated RMSNorm fused
-    # with the block quantization vs the normalization then the quantizer
+    # producer A/B on a transformer block's input: modulated RMSNorm / LayerNorm
+    # fused with the block quantization vs the normalization then the quantizer
     xr, rsc, rsh, yr, rq, rs = rms_buffers(dev)
-    w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)    # untimed first launches
+    for fn in (w8a8.rmsnorm_modulate_quantize_act, w8a8.layernorm_modulate_quantize_act):
+        fn(xr, rsc, rsh, 1e-6, rq, rs)
     w8a8.rmsnorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)
-    torch.cuda.synchronize()
-    w8a8.layernorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)
     w8a8.layernorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)
     torch.cuda.synchronize()
-    rt = {"fused": [], "norm": [], "quantize": [], "ln_fused": [], "ln_norm": []}
-    for i in range(args.steps):
-        for key, fn in (("fused", lambda: w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)),
-                        ("norm", lambda: w8a8.rmsnorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)),
-                        ("quantize", lambda: w8a8.quantize_act(yr.view(RB * RL, RK), rq, rs)),
-                        ("ln_fused", lambda: w8a8.layernorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs)),
-                        ("ln_norm", lambda: w8a8.layernorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr))):
-            flush.amax()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            rt[key].append((a, b))
-    torch.cuda.synchronize()
-    rms_us = {k: sum(a.elapsed_time(b) for a, b in v) / args.steps * 1e3 for k, v in rt.items()}
+    rt = event_times({"fused": lambda: w8a8.rmsnorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs),
+                      "norm": lambda: w8a8.rmsnorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr),
+                      "quantize": lambda: w8a8.quantize_act(yr.view(RB * RL, RK), rq, rs),
+                      "ln_fused": lambda: w8a8.layernorm_modulate_quantize_act(xr, rsc, rsh, 1e-6, rq, rs),
+                      "ln_norm": lambda: w8a8.layernorm_modulate_bf16(xr, rsc, rsh, 1e-6, out=yr)},
+                     args.steps, flush=flush)
+    rms_us = {k: v["mean"] for k, v in rt.items()}
     del xr, rsc, rsh, yr, rq, rs
     log(f"RMSNorm producer A/B ({RB}x{RL}x{RK}): fused {rms_us['fused']:.1f} us "
         f"({RMS_BYTES / rms_us['fused'] / 1e3:.0f} GB/s algorithmic) vs norm {rms_us['norm']:.1f} + "
         f"quantize {rms_us['quantize']:.1f} us")
     log(f"LayerNorm producer A/B: fused {rms_us['ln_fused']:.1f} us vs norm {rms_us['ln_norm']:.1f} + "
         f"quantize {rms_us['quantize']:.1f} us")
-
-    # a transformer block's W8A8 work (attention itself excluded), 4 x 8192
-    # tokens x 4096, 32 heads of 128, MLP 16384: every fusion of the library
-    # in place vs the same steps unfused
-    blk_us = block_slice_ab(w8a8, dev, args.steps)
-    log(f"block slice: fused {blk_us['fused']:.1f} us vs unfused {blk_us['unfused']:.1f} us per block")
 
     # A/B: the post-scale form (per-row / per-channel scales applied once,
     # INT32 over all of K) on the same inputs and shape
@@ -730,26 +934,14 @@ def main():
     w8a8.quantize_rows(x, qxp, sxp)
     w8a8.gemm_postscale(qxp, sxp, qwp, swp, out=y)     # untimed first launch
     torch.cuda.synchronize()
-    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        evp[i][0].record()
-        w8a8.gemm_postscale(qxp, sxp, qwp, swp, out=y)
-        evp[i][1].record()
-    torch.cuda.synchronize()
-    ps_gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evp) / args.steps
-    # row quantization timed like the block one: after the same read flush
-    pq = []
-    for i in range(args.steps):
-        flush.amax()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        w8a8.quantize_rows(x, qxp, sxp)
-        b.record()
-        pq.append((a, b))
-    torch.cuda.synchronize()
-    ps_quant_ms = sum(a.elapsed_time(b) for a, b in pq) / args.steps
-    del qxp, qwp, flush
+    ps_gemm_ms = event_times({"g": lambda: w8a8.gemm_postscale(qxp, sxp, qwp, swp, out=y)},
+                             args.steps)["g"]["mean"] / 1e3
+    ps_quant_ms = event_times({"q": lambda: w8a8.quantize_rows(x, qxp, sxp)}, args.steps, flush=flush)["q"]["mean"] / 1e3
+    del qxp, qwp
     vendor = vendor_int8_context(qx, qw)
+
+    extra = extras(w8a8, dev, args, x, y, qx, sx, qw, sw, flush) if args.extras else None
+    del flush_buf
 
     gemm_tops = GEMM_OPS / (gemm_ms * 1e-3) / 1e12
     quant_gbs = QUANT_BYTES / (quant_ms * 1e-3) / 1e9
@@ -765,6 +957,13 @@ def main():
         cpu = cpu_baseline(d)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GOPS on {cpu['cores']} threads, {cpu['seconds']} s")
 
+    configs["attention_projection"] = {
+        "shape": [M, N, K], "gemm_us": round(gemm_ms * 1e3, 2), "gemm_tops": round(gemm_tops, 1),
+        "gemm_frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4),
+        "quantize_us": round(quant_ms * 1e3, 2), "quantize_gbs": round(quant_gbs, 1),
+        "quantize_frac_of_hbm": round(quant_gbs / PEAK_HBM_GBS, 4),
+        "note": "the headline workload (the step); oracle: cpu_baseline"}
+
     traffic = load_traffic()
     out = {
         "metric": METRIC,
@@ -773,6 +972,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -801,7 +1001,9 @@ def main():
                               "unit": "GB/s", "frac": round(quant_gbs / PEAK_HBM_GBS, 4),
                               "traffic": load_traffic(QUANT_TRAFFIC_FILE, QUANT_SOURCE),
                               "algorithmic_bytes": QUANT_BYTES},
+        "clock": clock,
         "cpu_baseline": cpu,
+        "configs": configs,
         "postscale_ab": {"note": "post-scale form on the same shape (not the headline path)",
                          "gemm_us": round(ps_gemm_ms * 1e3, 2),
                          "gemm_tops": round(GEMM_OPS / (ps_gemm_ms * 1e-3) / 1e12, 1),
@@ -824,45 +1026,9 @@ def main():
                         "us": round(qk_us, 2), "gbs": round(QK_BYTES / qk_us / 1e3, 1),
                         "frac_of_hbm": round(QK_BYTES / qk_us / 1e3 / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": QK_BYTES},
-        "gated_residual_ab": {"note": "gated residual update h + gate * o of the attention projection's output "
-                                      "(4 batch entries of 8192 tokens) in the block GEMM's epilogue vs the GEMM "
-                                      "then the update kernel (not part of a step)",
-                              "shape": [M, N, K], "batch_entries": RES_B,
-                              "fused_us": round(res_us["fused"], 2),
-                              "fused_tops": round(GEMM_OPS / (res_us["fused"] * 1e-6) / 1e12, 1),
-                              "unfused_gemm_us": round(res_us["gemm"], 2),
-                              "unfused_update_us": round(res_us["update"], 2),
-                              "update_gbs": round(RES_UPDATE_BYTES / res_us["update"] / 1e3, 1),
-                              "speedup": round((res_us["gemm"] + res_us["update"]) / res_us["fused"], 3)},
-        "block_slice_ab": {"note": "one transformer block's W8A8 work, attention excluded (4 x 8192 tokens x 4096, "
-                                   "32 heads of 128, MLP 16384): modulated RMSNorm -> Q/K/V group -> rotary + INT8 "
-                                   "Q/K -> output projection + gated residual -> modulated RMSNorm -> MLP up -> "
-                                   "GELU -> MLP down + gated residual; fused = every producer in the next quantizer "
-                                   "and every residual update in the GEMM epilogue, unfused = the same steps through "
-                                   "bf16 tensors; V stands in for the attention output (not part of a step)",
-                           "fused_us": round(blk_us["fused"], 1), "unfused_us": round(blk_us["unfused"], 1),
-                           "speedup": round(blk_us["unfused"] / blk_us["fused"], 3)},
-        "v_fp8_quantize": {"note": "attention V in FP8 E4M3 (s = max-abs/448 per 128 tokens x head) from the "
-                                   "third column slice of the fused Q/K/V output -> head-major codes (not part "
-                                   "of a step)",
-                           "us": round(v_us, 2), "gbs": round(QK_BYTES / v_us / 1e3, 1),
-                           "frac_of_hbm": round(QK_BYTES / v_us / 1e3 / PEAK_HBM_GBS, 4),
-                           "algorithmic_bytes": QK_BYTES},
-        "rope_qk_ab": {"note": "split-halves rotary embedding fused into the INT8 Q/K quantizer vs rotation "
-                               "to bf16 then quantization, per Q or K tensor of the video self-attention "
-                               "(not part of a step); tables fp32 [tokens, head_dim/2]",
-                       "shape": {"tokens": AL, "heads": AH, "head_dim": AD, "row_stride": 3 * AH * AD,
-                                 "table_grid": list(ROPE_GRID)},
-                       "fused_us": round(rope_us["fused"], 2),
-                       "fused_gbs_algorithmic": round(ROPE_QK_BYTES / rope_us["fused"] / 1e3, 1),
-                       "fused_frac_of_hbm": round(ROPE_QK_BYTES / rope_us["fused"] / 1e3 / PEAK_HBM_GBS, 4),
-                       "algorithmic_bytes": ROPE_QK_BYTES,
-                       "unfused_rotate_us": round(rope_us["rotate"], 2),
-                       "unfused_quantize_us": round(rope_us["quantize"], 2),
-                       "speedup": round((rope_us["rotate"] + rope_us["quantize"]) / rope_us["fused"], 3)},
         "rmsnorm_producer_ab": {"note": "transformer-block input: modulated RMSNorm fused with the 128x128 "
                                         "block quantize vs the normalization then the quantizer (not part of a "
-                                        "step); the fused entry reads x twice (row norms, then the blocks)",
+                                        "step)",
                                 "shape": [RB, RL, RK],
                                 "fused_us": round(rms_us["fused"], 2),
                                 "fused_gbs_algorithmic": round(RMS_BYTES / rms_us["fused"] / 1e3, 1),
@@ -871,12 +1037,12 @@ def main():
                                 "unfused_norm_us": round(rms_us["norm"], 2),
                                 "unfused_quantize_us": round(rms_us["quantize"], 2),
                                 "speedup": round((rms_us["norm"] + rms_us["quantize"]) / rms_us["fused"], 3)},
-        "layernorm_producer_ab": {"note": "the same input with the modulated layer normalization (mean and "
-                                          "variance, two passes over each row for its statistics) fused with "
+        "layernorm_producer_ab": {"note": "the same input with the modulated layer normalization fused with "
                                           "the 128x128 block quantize vs the normalization then the quantizer",
                                   "shape": [RB, RL, RK],
                                   "fused_us": round(rms_us["ln_fused"], 2),
                                   "fused_gbs_algorithmic": round(RMS_BYTES / rms_us["ln_fused"] / 1e3, 1),
+                                  "fused_frac_of_hbm": round(RMS_BYTES / rms_us["ln_fused"] / 1e3 / PEAK_HBM_GBS, 4),
                                   "algorithmic_bytes": RMS_BYTES,
                                   "unfused_norm_us": round(rms_us["ln_norm"], 2),
                                   "unfused_quantize_us": round(rms_us["quantize"], 2),
@@ -891,7 +1057,10 @@ def main():
                         "unfused_gelu_us": round(prod_us["gelu"], 2),
                         "unfused_quantize_us": round(prod_us["quantize"], 2),
                         "speedup": round((prod_us["gelu"] + prod_us["quantize"]) / prod_us["fused"], 3)},
+        "run_seconds": round(time.perf_counter() - t_start, 1),
     }
+    if extra:
+        out["extras"] = extra
     print(json.dumps(out), flush=True)
 
 
