@@ -40,6 +40,7 @@ and ``W8A8Linear.forward_gated_residual(x, h, gate)``.
 from __future__ import annotations
 
 import ctypes
+import os
 
 import torch
 
@@ -53,10 +54,18 @@ __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "rout
            "POSTSCALE_MAX_K", "gelu_bf16", "gelu_quantize_act", "quantize_qk",
            "rmsnorm_modulate_bf16", "rmsnorm_modulate_quantize_act", "layernorm_modulate_bf16",
            "layernorm_modulate_quantize_act", "rope_bf16", "rope_quantize_qk", "quantize_v_fp8",
-           "gated_residual", "gemm_blockscale_gated_residual",
+           "gated_residual", "gemm_blockscale_gated_residual", "linear_gelu", "linear_modulated",
+           "producer_workspace_bytes", "force_fallback",
            "PATH_INT8", "PATH_BF16", "DTYPE_BF16", "DTYPE_FP16", "DTYPE_FP32", "BLOCK", "EXPORTS"]
 
 _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32: DTYPE_FP32}
+
+
+def force_fallback() -> bool:
+    """True when the environment sets W8A8_FORCE_FALLBACK=1 (a test switch):
+    the guarded entry points are then called without the quantized weight,
+    so the library's router sends every call to the bf16 fallback."""
+    return os.environ.get("W8A8_FORCE_FALLBACK", "") == "1"
 
 
 def _need_cuda(name, t, dtype=None):
@@ -423,6 +432,8 @@ def _guarded(fn_name, ws_bytes, x, w, qw, sw, bias, out, workspace):
     M = x2.shape[0]
     if (qw is None) != (sw is None):
         raise ValueError("qw and sw go together")
+    if force_fallback():
+        qw = sw = None
     if qw is not None:
         _need_cuda("qw", qw, torch.int8)
         _need_cuda("sw", sw, torch.float32)
@@ -508,6 +519,78 @@ def debug_kblock_partials(qx, qw, m0: int, mt: int, n0: int, nt: int):
     return out
 
 
+def producer_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().w8a8_linear_producer_workspace_bytes(M, K))
+
+
+def _producer_common(w, qw, sw, bias, M, K, out, workspace, device):
+    _need_cuda("w", w, torch.bfloat16)
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("the input and w disagree on K")
+    if (qw is None) != (sw is None):
+        raise ValueError("qw and sw go together")
+    if force_fallback():
+        qw = sw = None
+    if qw is not None:
+        _need_cuda("qw", qw, torch.int8)
+        _need_cuda("sw", sw, torch.float32)
+    if bias is not None:
+        _need_cuda("bias", bias, torch.bfloat16)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    _need_cuda("out", out, torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out must have M x N elements")
+    need = producer_workspace_bytes(M, K)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _need_cuda("workspace", workspace)
+    return N, qw, sw, out, workspace, need
+
+
+def linear_gelu(u, w, qw=None, sw=None, bias=None, out=None, workspace=None):
+    """Guarded ``GELU(u) @ w.T (+ bias)`` for bf16 u [..., K]: the library
+    fuses the exact GELU into the INT8 path's activation quantization, or
+    runs GELU then the bf16 fallback; returns (Y bf16 [..., N], path)."""
+    _need_cuda("u", u, torch.bfloat16)
+    K = w.shape[1]
+    if u.shape[-1] != K:
+        raise ValueError(f"last dimension of u must be {K}")
+    u2 = u.reshape(-1, K)
+    if not u2.is_contiguous():
+        u2 = u2.contiguous()
+    M = u2.shape[0]
+    N, qw, sw, out, workspace, need = _producer_common(w, qw, sw, bias, M, K, out, workspace, u.device)
+    path = ctypes.c_int(-1)
+    check("w8a8_linear_gelu",
+          lib().w8a8_linear_gelu(_ptr(u2), M, K, N, _ptr(w), _ptr(qw), _ptr(sw), _ptr(bias), _ptr(out),
+                                 _ptr(workspace), need, _stream(u.device), ctypes.byref(path)))
+    return out.reshape(*u.shape[:-1], N), path.value
+
+
+def linear_modulated(x, scale, shift, w, qw=None, sw=None, bias=None, eps: float = 1e-6, norm: str = "rms",
+                     out=None, workspace=None):
+    """Guarded ``norm_modulate(x, scale, shift, eps) @ w.T (+ bias)`` for bf16
+    x [B, L, K] (or [L, K]) with scale, shift [B, K] (``norm``: "rms" or
+    "layer"): the normalization is fused into the INT8 path's activation
+    quantization, or runs alone before the bf16 fallback; returns
+    (Y bf16 [..., N], path)."""
+    if norm not in ("rms", "layer"):
+        raise ValueError("norm must be 'rms' or 'layer'")
+    x3, B, L, K = _modulation_args(x, scale, shift)
+    M = B * L
+    N, qw, sw, out, workspace, need = _producer_common(w, qw, sw, bias, M, K, out, workspace, x.device)
+    fn = "w8a8_linear_rmsnorm_modulate" if norm == "rms" else "w8a8_linear_layernorm_modulate"
+    path = ctypes.c_int(-1)
+    check(fn, getattr(lib(), fn)(_ptr(x3), B, L, K, _ptr(scale), _ptr(shift), float(eps), N, _ptr(w), _ptr(qw),
+                                 _ptr(sw), _ptr(bias), _ptr(out), _ptr(workspace), need, _stream(x.device),
+                                 ctypes.byref(path)))
+    return out.view(*x.shape[:-1], N), path.value
+
+
 class W8A8Linear(torch.nn.Module):
     """Linear layer on the guarded W8A8 path.
 
@@ -537,6 +620,7 @@ class W8A8Linear(torch.nn.Module):
             elif K <= POSTSCALE_MAX_K:
                 self.qweight, self.wscale = quantize_rows(weight)
         self._workspace = None
+        self._pworkspace = None
         self.last_path = None
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
@@ -552,64 +636,46 @@ class W8A8Linear(torch.nn.Module):
                                workspace=self._workspace)
         return y
 
+    def _producer_workspace(self, M, K, device):
+        need = producer_workspace_bytes(M, K)
+        if self._pworkspace is None or self._pworkspace.numel() < need or self._pworkspace.device != device:
+            self._pworkspace = torch.empty(need, dtype=torch.uint8, device=device)
+        return self._pworkspace
+
+    def _block_weights(self):
+        # the producer entries implement the block form only
+        return (self.qweight, self.wscale) if self.scaling == "block" else (None, None)
+
     def forward_gelu(self, y: torch.Tensor) -> torch.Tensor:
         """``self(GELU(y))`` for a bf16 ``y`` [..., K]: the second linear of an
-        MLP with the activation fused into its input quantization when the
-        INT8 block path applies; otherwise GELU runs alone and ``forward``
-        takes its own guarded path."""
-        N, K = self.weight.shape
-        _need_cuda("y", y, torch.bfloat16)
-        if y.shape[-1] != K:
-            raise ValueError(f"last dimension of y must be {K}")
-        M = y.numel() // K
-        fused = (self.scaling == "block" and self.qweight is not None and M > 0 and K <= BLOCK_MAX_K
-                 and route(torch.bfloat16, M, K, N, True) == PATH_INT8 and y.data_ptr() % 16 == 0)
-        if not fused:
+        MLP, one guarded library call (w8a8_linear_gelu) that fuses the
+        activation into the input quantization on the INT8 path."""
+        if self.scaling != "block":
             return self.forward(gelu_bf16(y))
-        need = workspace_bytes(M, K)
-        if self._workspace is None or self._workspace.numel() < need or self._workspace.device != y.device:
-            self._workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
-        s_off = (M * K + 255) // 256 * 256
-        q = self._workspace[:M * K].view(torch.int8).view(M, K)
-        s = self._workspace[s_off:s_off + 4 * (M // BLOCK) * (K // BLOCK)].view(torch.float32)
-        gelu_quantize_act(y.reshape(M, K), q, s.view(M // BLOCK, K // BLOCK))
-        out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
-        self.last_path = PATH_INT8
-        return out.view(*y.shape[:-1], N)
-
+        K = self.weight.shape[1]
+        qw, sw = self._block_weights()
+        out, self.last_path = linear_gelu(y, self.weight, qw, sw, self.bias,
+                                          workspace=self._producer_workspace(y.numel() // K if K else 0, K,
+                                                                             y.device))
+        return out
 
     def forward_modulated(self, x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
                           eps: float = 1e-6, norm: str = "rms") -> torch.Tensor:
         """``self(rmsnorm_modulate_bf16(x, scale, shift, eps))`` for bf16 x
-        [B, L, K] (``norm="layer"``: ``layernorm_modulate_bf16``): the
-        modulated normalization fused into the input quantization when the
-        INT8 block path applies; otherwise it runs alone and ``forward``
-        takes its own guarded path."""
+        [B, L, K] (``norm="layer"``: ``layernorm_modulate_bf16``): one guarded
+        library call that fuses the normalization into the input quantization
+        on the INT8 path."""
         if norm not in ("rms", "layer"):
             raise ValueError("norm must be 'rms' or 'layer'")
-        alone, fused_fn = ((rmsnorm_modulate_bf16, rmsnorm_modulate_quantize_act) if norm == "rms"
-                           else (layernorm_modulate_bf16, layernorm_modulate_quantize_act))
-        N, K = self.weight.shape
-        x3, B, L, Kx = _modulation_args(x, scale, shift)
-        if Kx != K:
-            raise ValueError(f"last dimension of x must be {K}")
-        M = B * L
-        fused = (self.scaling == "block" and self.qweight is not None and K <= BLOCK_MAX_K
-                 and route(torch.bfloat16, M, K, N, True) == PATH_INT8 and x3.data_ptr() % 16 == 0
-                 and scale.data_ptr() % 16 == 0 and shift.data_ptr() % 16 == 0)
-        if not fused:
+        if self.scaling != "block":
+            alone = rmsnorm_modulate_bf16 if norm == "rms" else layernorm_modulate_bf16
             return self.forward(alone(x, scale, shift, eps))
-        need = workspace_bytes(M, K)
-        if self._workspace is None or self._workspace.numel() < need or self._workspace.device != x.device:
-            self._workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-        s_off = (M * K + 255) // 256 * 256
-        q = self._workspace[:M * K].view(torch.int8).view(M, K)
-        s = self._workspace[s_off:s_off + 4 * (M // BLOCK) * (K // BLOCK)].view(torch.float32)
-        fused_fn(x3, scale, shift, eps, q, s.view(M // BLOCK, K // BLOCK))
-        out = gemm_blockscale(q, s.view(M // BLOCK, K // BLOCK), self.qweight, self.wscale, self.bias)
-        self.last_path = PATH_INT8
-        return out.view(*x.shape[:-1], N)
-
+        K = self.weight.shape[1]
+        qw, sw = self._block_weights()
+        ws = self._producer_workspace(x.numel() // K if K else 0, K, x.device)
+        out, self.last_path = linear_modulated(x, scale, shift, self.weight, qw, sw, self.bias, eps, norm,
+                                               workspace=ws)
+        return out
 
     def forward_gated_residual(self, x: torch.Tensor, h: torch.Tensor, gate: torch.Tensor,
                                out=None) -> torch.Tensor:
@@ -633,14 +699,15 @@ class W8A8Linear(torch.nn.Module):
         _need_cuda("out", out, torch.bfloat16)
         if out.numel() != M * N:
             raise ValueError("out must have the output's M x N elements")
-        need = workspace_bytes(M, K) if self.qweight is not None else 0
+        qw, sw = (None, None) if force_fallback() else (self.qweight, self.wscale)
+        need = workspace_bytes(M, K) if qw is not None else 0
         if need and (self._workspace is None or self._workspace.numel() < need
                      or self._workspace.device != x.device):
             self._workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
         path = ctypes.c_int(-1)
         check("w8a8_linear_gated_residual",
               lib().w8a8_linear_gated_residual(_ptr(x2), _DTYPES[x2.dtype], M, K, N, _ptr(self.weight),
-                                               _ptr(self.qweight), _ptr(self.wscale), _ptr(self.bias), _ptr(h),
+                                               _ptr(qw), _ptr(sw), _ptr(self.bias), _ptr(h),
                                                _ptr(gate), L, _ptr(out), _ptr(self._workspace) if need else None,
                                                need, _stream(x.device), ctypes.byref(path)))
         self.last_path = path.value

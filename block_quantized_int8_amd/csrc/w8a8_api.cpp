@@ -59,6 +59,33 @@ int rmsnorm_args(const void *x, int64_t B, int64_t L, int64_t K, const void *sca
     return W8A8_OK;
 }
 
+// Final path of a guarded linear before its workspace is looked at: the
+// route (dtype, shapes, quantized weight), the GEMM's K limit, then the
+// alignment the INT8 kernels need on x, y, qw (16 bytes), sw (sw_align) and
+// bias (8); any miss takes the bf16 fallback.  y may be null when the caller
+// checks it separately.
+int guarded_path(int x_dtype, int64_t M, int64_t K, int64_t N, const void *x, const void *y, const int8_t *qw,
+                 const float *sw, uintptr_t sw_align, const void *bias, int64_t max_k) {
+    int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
+    if (path == W8A8_PATH_INT8 && K > max_k) path = W8A8_PATH_BF16;
+    if (path == W8A8_PATH_INT8 && (!aligned(x, 16) || (y && !aligned(y, 16)) || !aligned(qw, 16) ||
+                                   !aligned(sw, sw_align) || !aligned(bias, 8)))
+        path = W8A8_PATH_BF16;
+    return path;
+}
+
+// Workspace checks of a call that takes the INT8 path: present, large
+// enough and device memory (else W8A8_ERR_INVALID_ARG); a workspace that is
+// not 16-byte aligned sends the call to the fallback instead.
+int int8_workspace(int &path, const int8_t *qw, const float *sw, void *workspace, size_t workspace_bytes,
+                   size_t need) {
+    if (path != W8A8_PATH_INT8) return W8A8_OK;
+    if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
+    if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(workspace, 16)) path = W8A8_PATH_BF16;
+    return W8A8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,18 +141,10 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, con
         (bias_bf16 && !is_device_ptr(bias_bf16)))
         return W8A8_ERR_INVALID_ARG;
 
-    int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
-    if (path == W8A8_PATH_INT8 && K > W8A8_BLOCK_MAX_K) path = W8A8_PATH_BF16;
-    if (path == W8A8_PATH_INT8) {
-        const size_t need = w8a8_linear_workspace_bytes(M, K);
-        if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
-        if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace))
-            return W8A8_ERR_INVALID_ARG;
-        // the INT8 kernels use 16-byte loads/stores; otherwise fall back
-        if (!aligned(x, 16) || !aligned(y_bf16, 16) || !aligned(qw, 16) || !aligned(workspace, 16) ||
-            !aligned(sw, 4) || !aligned(bias_bf16, 8))
-            path = W8A8_PATH_BF16;
-    }
+    // the INT8 kernels use 16-byte loads/stores: misaligned operands fall back
+    int path = guarded_path(x_dtype, M, K, N, x, y_bf16, qw, sw, 4, bias_bf16, W8A8_BLOCK_MAX_K);
+    const int ws_status = int8_workspace(path, qw, sw, workspace, workspace_bytes, w8a8_linear_workspace_bytes(M, K));
+    if (ws_status != W8A8_OK) return ws_status;
     if (path_out) *path_out = path;
 
     if (path == W8A8_PATH_INT8) {
@@ -206,16 +225,10 @@ int w8a8_linear_gated_residual(const void *x, int x_dtype, int64_t M, int64_t K,
         !is_device_ptr(gate_bf16) || (bias_bf16 && !is_device_ptr(bias_bf16)))
         return W8A8_ERR_INVALID_ARG;
 
-    int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
-    if (path == W8A8_PATH_INT8 && (K > W8A8_BLOCK_MAX_K || M > INT32_MAX)) path = W8A8_PATH_BF16;
-    if (path == W8A8_PATH_INT8) {
-        const size_t need = w8a8_linear_workspace_bytes(M, K);
-        if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
-        if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace)) return W8A8_ERR_INVALID_ARG;
-        if (!aligned(x, 16) || !aligned(qw, 16) || !aligned(workspace, 16) || !aligned(sw, 4) ||
-            !aligned(bias_bf16, 8))
-            path = W8A8_PATH_BF16;
-    }
+    int path = guarded_path(x_dtype, M, K, N, x, nullptr, qw, sw, 4, bias_bf16, W8A8_BLOCK_MAX_K);
+    if (path == W8A8_PATH_INT8 && M > INT32_MAX) path = W8A8_PATH_BF16;
+    const int ws_status = int8_workspace(path, qw, sw, workspace, workspace_bytes, w8a8_linear_workspace_bytes(M, K));
+    if (ws_status != W8A8_OK) return ws_status;
     if (path_out) *path_out = path;
 
     if (path == W8A8_PATH_INT8) {
@@ -287,16 +300,10 @@ int w8a8_linear_postscale(const void *x, int x_dtype, int64_t M, int64_t K, int6
     if (!is_device_ptr(x) || !is_device_ptr(w_bf16) || !is_device_ptr(y_bf16) ||
         (bias_bf16 && !is_device_ptr(bias_bf16)))
         return W8A8_ERR_INVALID_ARG;
-    int path = w8a8_route(x_dtype, M, K, N, qw != nullptr);
-    if (path == W8A8_PATH_INT8 && K > W8A8_POSTSCALE_MAX_K) path = W8A8_PATH_BF16;
-    if (path == W8A8_PATH_INT8) {
-        const size_t need = w8a8_linear_postscale_workspace_bytes(M, K);
-        if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
-        if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace)) return W8A8_ERR_INVALID_ARG;
-        if (!aligned(x, 16) || !aligned(y_bf16, 16) || !aligned(qw, 16) || !aligned(workspace, 16) ||
-            !aligned(sw, 16) || !aligned(bias_bf16, 8))
-            path = W8A8_PATH_BF16;
-    }
+    int path = guarded_path(x_dtype, M, K, N, x, y_bf16, qw, sw, 16, bias_bf16, W8A8_POSTSCALE_MAX_K);
+    const int ws_status =
+        int8_workspace(path, qw, sw, workspace, workspace_bytes, w8a8_linear_postscale_workspace_bytes(M, K));
+    if (ws_status != W8A8_OK) return ws_status;
     if (path_out) *path_out = path;
     if (path == W8A8_PATH_INT8) {
         int8_t *qx = static_cast<int8_t *>(workspace);
@@ -466,6 +473,112 @@ int w8a8_layernorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t 
     return hip_status(w8a8::launch_modulate_quantize(x, stats_ws, true, B * L, L, K,
                                                      static_cast<const uint16_t *>(scale_bf16),
                                                      static_cast<const uint16_t *>(shift_bf16), qx, sx, stream));
+}
+
+size_t w8a8_linear_producer_workspace_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    const size_t stats = round256((size_t)M * 2 * sizeof(float));
+    const size_t fallback = round256((size_t)M * (size_t)K * 2) + stats;
+    const size_t int8 = w8a8_linear_workspace_bytes(M, K) + stats;
+    return fallback > int8 ? fallback : int8;
+}
+
+// Workspace of the producer linears: on the INT8 path qx and sx (as in
+// w8a8_linear) then the per-row statistics; on the fallback the producer's
+// bf16 output [M, K] then the statistics.
+static float *producer_stats(void *workspace, int path, int64_t M, int64_t K) {
+    const size_t off = path == W8A8_PATH_INT8 ? w8a8_linear_workspace_bytes(M, K) : round256((size_t)M * (size_t)K * 2);
+    return reinterpret_cast<float *>(static_cast<char *>(workspace) + off);
+}
+
+int w8a8_linear_gelu(const void *u_bf16, int64_t M, int64_t K, int64_t N, const void *w_bf16, const int8_t *qw,
+                     const float *sw, const void *bias_bf16, void *y_bf16, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream, int *path_out) {
+    if (!u_bf16 || !w_bf16 || !y_bf16 || M <= 0 || K <= 0 || N <= 0) return W8A8_ERR_INVALID_ARG;
+    if ((qw == nullptr) != (sw == nullptr)) return W8A8_ERR_INVALID_ARG;
+    if (M > INT64_MAX / K) return W8A8_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < w8a8_linear_producer_workspace_bytes(M, K)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(u_bf16, 2) || !aligned(workspace, 16)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(u_bf16) || !is_device_ptr(w_bf16) || !is_device_ptr(y_bf16) || !is_device_ptr(workspace) ||
+        (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+    const int64_t max_k = W8A8_GELU_QUANT_MAX_K < W8A8_BLOCK_MAX_K ? W8A8_GELU_QUANT_MAX_K : W8A8_BLOCK_MAX_K;
+    int path = guarded_path(W8A8_DTYPE_BF16, M, K, N, u_bf16, y_bf16, qw, sw, 4, bias_bf16, max_k);
+    if (path == W8A8_PATH_INT8 && (!is_device_ptr(qw) || !is_device_ptr(sw))) return W8A8_ERR_INVALID_ARG;
+    if (path_out) *path_out = path;
+    const uint16_t *u = static_cast<const uint16_t *>(u_bf16);
+    const uint16_t *bias = static_cast<const uint16_t *>(bias_bf16);
+    uint16_t *y = static_cast<uint16_t *>(y_bf16);
+    if (path == W8A8_PATH_INT8) {
+        int8_t *qx = static_cast<int8_t *>(workspace);
+        float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) + round256((size_t)M * (size_t)K));
+        hipError_t e = w8a8::launch_gelu_quantize_block(u, M, K, qx, sx, stream);
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(w8a8::launch_gemm_i8_blockscale(qx, sx, qw, sw, bias, M, N, K, y, stream));
+    }
+    uint16_t *g = static_cast<uint16_t *>(workspace);
+    hipError_t e = w8a8::launch_gelu_bf16(u, M * K, g, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(w8a8::launch_gemm_bf16(g, W8A8_DTYPE_BF16, static_cast<const uint16_t *>(w_bf16), bias, M, N,
+                                             K, y, stream));
+}
+
+// The two modulated-normalization linears share everything but the
+// statistic kernel and the centring.
+static int linear_modulated(bool layer, const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                            const void *shift_bf16, double eps, int64_t N, const void *w_bf16, const int8_t *qw,
+                            const float *sw, const void *bias_bf16, void *y_bf16, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream, int *path_out) {
+    if (!w_bf16 || !y_bf16 || N <= 0 || !workspace) return W8A8_ERR_INVALID_ARG;
+    if ((qw == nullptr) != (sw == nullptr)) return W8A8_ERR_INVALID_ARG;
+    // the statistics pointer only has to be non-null and aligned here; the real one follows the path
+    const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, static_cast<const float *>(workspace));
+    if (st != W8A8_OK) return st;
+    const int64_t M = B * L;
+    if (workspace_bytes < w8a8_linear_producer_workspace_bytes(M, K)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(workspace, 16)) return W8A8_ERR_UNSUPPORTED;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(scale_bf16) || !is_device_ptr(shift_bf16) || !is_device_ptr(w_bf16) ||
+        !is_device_ptr(y_bf16) || !is_device_ptr(workspace) || (bias_bf16 && !is_device_ptr(bias_bf16)))
+        return W8A8_ERR_INVALID_ARG;
+    int path = guarded_path(W8A8_DTYPE_BF16, M, K, N, x_bf16, y_bf16, qw, sw, 4, bias_bf16, W8A8_BLOCK_MAX_K);
+    if (path == W8A8_PATH_INT8 && (!is_device_ptr(qw) || !is_device_ptr(sw))) return W8A8_ERR_INVALID_ARG;
+    if (path_out) *path_out = path;
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    const uint16_t *scale = static_cast<const uint16_t *>(scale_bf16), *shift = static_cast<const uint16_t *>(shift_bf16);
+    const uint16_t *bias = static_cast<const uint16_t *>(bias_bf16);
+    uint16_t *y = static_cast<uint16_t *>(y_bf16);
+    float *stats = producer_stats(workspace, path, M, K);
+    hipError_t e = layer ? w8a8::launch_ln_rows(x, M, K, eps, stats, stream)
+                         : w8a8::launch_rms_rows(x, M, K, eps, stats, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (path == W8A8_PATH_INT8) {
+        int8_t *qx = static_cast<int8_t *>(workspace);
+        float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) + round256((size_t)M * (size_t)K));
+        e = w8a8::launch_modulate_quantize(x, stats, layer, M, L, K, scale, shift, qx, sx, stream);
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(w8a8::launch_gemm_i8_blockscale(qx, sx, qw, sw, bias, M, N, K, y, stream));
+    }
+    uint16_t *g = static_cast<uint16_t *>(workspace);
+    e = w8a8::launch_modulate_bf16(x, stats, layer, M, L, K, scale, shift, g, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(w8a8::launch_gemm_bf16(g, W8A8_DTYPE_BF16, static_cast<const uint16_t *>(w_bf16), bias, M, N,
+                                             K, y, stream));
+}
+
+int w8a8_linear_rmsnorm_modulate(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                 const void *shift_bf16, double eps, int64_t N, const void *w_bf16, const int8_t *qw,
+                                 const float *sw, const void *bias_bf16, void *y_bf16, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream, int *path_out) {
+    return linear_modulated(false, x_bf16, B, L, K, scale_bf16, shift_bf16, eps, N, w_bf16, qw, sw, bias_bf16, y_bf16,
+                            workspace, workspace_bytes, stream, path_out);
+}
+
+int w8a8_linear_layernorm_modulate(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                   const void *shift_bf16, double eps, int64_t N, const void *w_bf16,
+                                   const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out) {
+    return linear_modulated(true, x_bf16, B, L, K, scale_bf16, shift_bf16, eps, N, w_bf16, qw, sw, bias_bf16, y_bf16,
+                            workspace, workspace_bytes, stream, path_out);
 }
 
 const char *w8a8_status_string(int status) {

@@ -117,15 +117,17 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
  *   workspace: >= w8a8_linear_workspace_bytes(M, K) bytes when the INT8
  *              path is taken (may be null/0 otherwise)
  *   path_out : if not null, receives the W8A8_PATH_* taken
- * INT8 path iff w8a8_route(...) == W8A8_PATH_INT8, K <= W8A8_BLOCK_MAX_K
- * and x, y, qw and the workspace are 16-byte aligned: then the activation
- * is quantized into the
- * workspace and w8a8_gemm_blockscale's computation runs.  Otherwise the bf16
- * fallback runs: Y = bf16( sum_k bf16(x[m,k]) * w[n,k] (+ bias[n]) ) with
- * fp32 accumulation; fp16/fp32 x is rounded to bf16 (nearest even) on load.
- * Never fails on dtype or shape: returns W8A8_ERR_INVALID_ARG only for null
- * required pointers, sizes <= 0, an unknown dtype, a host pointer, or a
- * workspace smaller than needed by the INT8 path.
+ * INT8 path iff w8a8_route(...) == W8A8_PATH_INT8, K <= W8A8_BLOCK_MAX_K,
+ * x, y and qw are 16-byte aligned, sw 4-byte and bias 8-byte aligned, and
+ * the workspace is 16-byte aligned: then the activation is quantized into
+ * the workspace and w8a8_gemm_blockscale's computation runs.  Otherwise the
+ * bf16 fallback runs: Y = bf16( sum_k bf16(x[m,k]) * w[n,k] (+ bias[n]) )
+ * with fp32 accumulation; fp16/fp32 x is rounded to bf16 (nearest even) on
+ * load.  The path is decided from dtype, shapes, qw and the operands'
+ * alignment first; only a call that takes the INT8 path needs the
+ * workspace.  Never fails on dtype or shape: returns W8A8_ERR_INVALID_ARG
+ * only for null required pointers, sizes <= 0, an unknown dtype, a host
+ * pointer, or (INT8 path) a missing or too small workspace.
  */
 int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
                 const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
@@ -282,6 +284,51 @@ int w8a8_layernorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64
 int w8a8_layernorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L, int64_t K,
                                          const void *scale_bf16, const void *shift_bf16, double eps,
                                          float *stats_ws, int8_t *qx, float *sx, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Guarded linears with their producer in front (the TurboT2VA paper's guard
+ * paragraph and fused-kernels paragraph together: the fused kernel runs when
+ * the INT8 path applies, else the unfused producer and the bf16 linear).
+ * The route is w8a8_linear's, taken on the producer's bf16 output [M, K]:
+ * INT8 iff M, K, N are multiples of 128, a quantized weight is given, K is
+ * within the fused quantizer's and the GEMM's limits and the input, y, qw
+ * (16 bytes), sw (4) and bias (8) are aligned.  The INT8 path runs the fused
+ * producer + block quantization into the workspace and the block GEMM (the
+ * result equals w8a8_linear on the producer's bf16 output, bit for bit); the
+ * fallback writes the producer's bf16 output into the workspace and runs the
+ * bf16 GEMM on it.  Both paths need the workspace (device memory, 16-byte
+ * aligned, w8a8_linear_producer_workspace_bytes(M, K) bytes, else
+ * W8A8_ERR_INVALID_ARG / W8A8_ERR_UNSUPPORTED).  path_out (nullable)
+ * receives the W8A8_PATH_* taken.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace of the producer linears: the larger of qx + sx and a bf16 [M, K]
+ * copy, plus 8 bytes of statistics per row, each part 256-byte aligned. */
+size_t w8a8_linear_producer_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * Y[M, N] = bf16(GELU(u)) [M, K] * W^T (+ bias): the MLP's second linear with
+ * the exact GELU of w8a8_gelu_bf16 in front; u bf16 [M, K] (2-byte aligned).
+ */
+int w8a8_linear_gelu(const void *u_bf16, int64_t M, int64_t K, int64_t N, const void *w_bf16, const int8_t *qw,
+                     const float *sw, const void *bias_bf16, void *y_bf16, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream, int *path_out);
+
+/*
+ * Y[B*L, N] = w8a8_rmsnorm_modulate_bf16(x, scale, shift, eps) * W^T (+ bias)
+ * (and the layer-normalization form): x bf16 [B*L, K], scale and shift
+ * [B, K], eps and the normalization's own requirements as documented for
+ * w8a8_rmsnorm_modulate_bf16 (K % 8 == 0 and 16-byte aligned x, scale and
+ * shift on both paths, else W8A8_ERR_UNSUPPORTED).
+ */
+int w8a8_linear_rmsnorm_modulate(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                 const void *shift_bf16, double eps, int64_t N, const void *w_bf16, const int8_t *qw,
+                                 const float *sw, const void *bias_bf16, void *y_bf16, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream, int *path_out);
+int w8a8_linear_layernorm_modulate(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
+                                   const void *shift_bf16, double eps, int64_t N, const void *w_bf16,
+                                   const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out);
 
 /* ---------------------------------------------------------------------------
  * Gated residual update (TurboT2VA paper, architecture-aware inference stack,

@@ -180,6 +180,30 @@ int main() {
     CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 200, p, p, 1e-6, f, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 256, p, p, 1e-6, f, nullptr, f, nullptr) ==
           W8A8_ERR_INVALID_ARG);
+    // the path is decided before the workspace: a misaligned x takes the fallback, so a missing
+    // workspace is not an error there (the call stops at the host-pointer check instead)
+    CHECK(w8a8_linear(pc + 2, 0, 128, 128, 128, p, q8, f, nullptr, p, nullptr, 0, nullptr, &path) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(path == -7);
+    // producer linears: workspace size, missing workspace, sizes, the normalization's own rules
+    const size_t pws = w8a8_linear_producer_workspace_bytes(256, 256);
+    CHECK(pws == 256 * 256 * 2 + 256 * 8 && w8a8_linear_producer_workspace_bytes(0, 256) == 0);
+    CHECK(w8a8_linear_producer_workspace_bytes(4000, 4096) == (size_t)4000 * 4096 * 2 + 32000);
+    CHECK(w8a8_linear_gelu(p, 256, 256, 256, p, q8, f, nullptr, p, p, pws - 1, nullptr, &path) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear_gelu(p, 256, 256, 256, p, q8, nullptr, nullptr, p, p, pws, nullptr, &path) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear_gelu(pc + 1, 256, 256, 256, p, q8, f, nullptr, p, p, pws, nullptr, &path) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_linear_gelu(p, 256, 256, 256, p, q8, f, nullptr, p, p, pws, nullptr, &path) ==
+          W8A8_ERR_INVALID_ARG);                                                                  // host memory
+    CHECK(w8a8_linear_rmsnorm_modulate(p, 2, 128, 256, p, p, 0.0, 256, p, q8, f, nullptr, p, p, pws, nullptr, &path) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear_rmsnorm_modulate(p, 2, 128, 252, p, p, 1e-6, 256, p, q8, f, nullptr, p, p, 1 << 20, nullptr,
+                                       &path) == W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_linear_layernorm_modulate(p, 2, 128, 256, p, p, 1e-6, 256, p, q8, f, nullptr, p, nullptr, 1 << 20,
+                                         nullptr, &path) == W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_linear_layernorm_modulate(p, 2, 128, 256, p, p, 1e-6, 256, p, q8, f, nullptr, p, p, 1 << 20, nullptr,
+                                         &path) == W8A8_ERR_INVALID_ARG);                         // host memory
+    CHECK(path == -7);
     std::printf("host sanitizer driver: ok\n");
     return 0;
 }
