@@ -2,9 +2,9 @@
 //
 //   Y[m, n] = bf16( sum_k bf16(x[m, k]) * w[n, k] (+ bias[n]) ), fp32 sums,
 //
-// for any M, N, K >= 1, with the retained bf16 weight copy (TurboT2VA paper,
-// architecture-aware inference stack, guard paragraph: unsupported dtypes or
-// shapes run a native BF16 linear on the kept BF16 weights).  fp16 and fp32
+// for any M, N, K >= 1, with the layer's bf16 weight (TurboT2VA paper,
+// architecture-aware inference stack, guard paragraph: a call the INT8 path
+// cannot take is computed in bf16 instead).  fp16 and fp32
 // inputs are rounded to bf16 (nearest even) as they are loaded.
 //
 // One workgroup (4 wavefronts) per 128x128 output tile, 64-deep K steps

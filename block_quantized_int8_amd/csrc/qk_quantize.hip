@@ -1,10 +1,9 @@
 // INT8 block quantization of attention queries or keys, rearranged from
 // sequence-major to head-major on the way, for gfx950.
 //
-// The TurboT2VA paper's sparse-attention adapter (architecture-aware
-// inference stack, sparse-attention paragraph) turns the sequence-major
-// query, key and value tensors into the layout of the sparse kernel and
-// quantizes query and key to INT8.  Here: input element (b, l, h, d) is
+// Source: TurboT2VA paper, architecture-aware inference stack, sparse-attention
+// paragraph (the attention's Q and K enter its kernel as INT8, in that
+// kernel's layout rather than token-major).  Here: input element (b, l, h, d) is
 // x[(b*L + l)*ld + h*D + d] (for example a column slice of a fused Q/K/V
 // projection's output, ld being its row stride); each (b, h) is cut into
 // blocks of 128 consecutive tokens (the last one may be shorter) and every

@@ -16,10 +16,10 @@
  *     inference stack, W8A8 linear paragraph -- there per row/channel; here
  *     per block, so the INT32 sum is exact within each 128-deep K-block and
  *     the block scales are applied once per K-block);
- *   - the guard: the INT8 path needs a BF16 input and M, K, N divisible by
- *     128; otherwise a BF16 linear runs on the retained BF16 weight copy
- *     (TurboT2VA paper, same section, guard paragraph; pchao.org summary,
- *     method overview and caveats).
+ *   - the guard: only a bf16 input whose M, K and N are multiples of 128
+ *     goes to INT8; any other call is computed in bf16 from the bf16 weight
+ *     the layer keeps beside its INT8 copy (TurboT2VA paper, same section,
+ *     guard paragraph; pchao.org summary, method overview and caveats).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE memory (HIP), row-major and contiguous.
@@ -109,7 +109,7 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
 /*
  * Guarded linear: Y[M, N] (bf16) = X[M, K] * W[N, K]^T (+ bias).
  *   x        : [M, K], dtype x_dtype (W8A8_DTYPE_*), M = flattened leading dims
- *   w_bf16   : retained bf16 weight [N, K] (required: the fallback uses it)
+ *   w_bf16   : the layer's bf16 weight [N, K] (required: the fallback uses it)
  *   qw, sw   : w8a8_quantize_weight outputs for w_bf16 (both null -> no
  *              INT8 path; exactly one null -> W8A8_ERR_INVALID_ARG)
  *   bias_bf16: [N] or null
@@ -375,10 +375,9 @@ int w8a8_linear_gated_residual(const void *x, int x_dtype, int64_t M, int64_t K,
 
 /* ---------------------------------------------------------------------------
  * INT8 query/key for the sparse attention (TurboT2VA paper, architecture-
- * aware inference stack, sparse-attention paragraph: query and key are
- * quantized to INT8, and the sequence-major tensors are rearranged into the
- * attention kernel's layout).  The attention kernel itself is not part of
- * this library.
+ * aware inference stack, sparse-attention paragraph: its kernel consumes Q
+ * and K as INT8 and in its own layout, not token-major).  The attention
+ * kernel itself is not part of this library.
  * ------------------------------------------------------------------------- */
 
 /*

@@ -19,7 +19,7 @@
  *       stack, W8A8 linear paragraph.  (There it is stated per row / per
  *       output channel; the block form takes the same rule per block.)
  *   - the guard (bf16 input, M, K, N multiples of 128, else a bf16 linear on
- *       the retained bf16 weight): TurboT2VA paper, same section, guard
+ *       the layer's bf16 weight): TurboT2VA paper, same section, guard
  *       paragraph; pchao.org summary of TurboT2VA, method overview and
  *       caveats lists.
  *
@@ -238,7 +238,7 @@ static double load_as_bf16(const void *x, int dtype, int64_t idx) {
 }
 
 /*
- * Native bf16 linear on the retained bf16 weight, any M, N, K >= 1:
+ * Native bf16 linear on the layer's bf16 weight, any M, N, K >= 1:
  * Y[m, n] = bf16( sum_k bf16(x[m, k]) * w[n, k] (+ bias[n]) ), fp64 sum.
  */
 int oracle_linear_bf16_rows(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
@@ -331,9 +331,9 @@ int oracle_linear_postscale_rows(const int8_t *qx, const float *sx, const int8_t
 /*
  * INT8 block quantization of an attention query or key tensor together with
  * the change from sequence-major to head-major layout (TurboT2VA paper,
- * architecture-aware inference stack, sparse-attention paragraph: the
- * adapter rearranges query, key and value into the sparse kernel's layout,
- * and query and key are quantized to INT8).  Input element (b, l, h, d) is
+ * architecture-aware inference stack, sparse-attention paragraph: Q and K
+ * reach the sparse kernel as INT8, in its layout instead of token-major).
+ * Input element (b, l, h, d) is
  * x[(b * L + l) * ld + h * D + d] (ld >= H * D, the row stride).  Each
  * (b, h) is cut into blocks of 128 consecutive tokens (the last one may be
  * shorter); per block a = max |x| over its tokens and all D dims (exact),
