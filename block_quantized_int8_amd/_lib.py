@@ -28,11 +28,12 @@ EXPORTS = (
     "w8a8_rope_quantize_qk", "w8a8_gated_residual", "w8a8_gemm_blockscale_gated_residual",
     "w8a8_linear_gated_residual", "w8a8_layernorm_modulate_bf16", "w8a8_layernorm_modulate_quantize_act",
     "w8a8_quantize_v_fp8", "w8a8_linear_producer_workspace_bytes", "w8a8_linear_gelu",
-    "w8a8_linear_rmsnorm_modulate", "w8a8_linear_layernorm_modulate",
+    "w8a8_linear_rmsnorm_modulate", "w8a8_linear_layernorm_modulate", "w8a8_linear_noalloc",
 )
 POSTSCALE_MAX_K = 133120
 BLOCK_MAX_K = 4194304
 GELU_QUANT_MAX_K = 8388480
+NOALLOC_SCRATCH_BYTES = 33554432 + 65536
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -94,6 +95,8 @@ def lib():
     L.w8a8_linear_rmsnorm_modulate.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _I64, _P, _P, _P, _P,
                                                _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(ctypes.c_int)]
     L.w8a8_linear_layernorm_modulate.argtypes = L.w8a8_linear_rmsnorm_modulate.argtypes
+    L.w8a8_linear_noalloc.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P,
+                                      ctypes.POINTER(ctypes.c_int)]
     L.w8a8_status_string.argtypes = [ctypes.c_int]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
@@ -104,7 +107,8 @@ def lib():
               "w8a8_rope_quantize_qk", "w8a8_rmsnorm_modulate_bf16", "w8a8_rmsnorm_modulate_quantize_act",
               "w8a8_gated_residual", "w8a8_gemm_blockscale_gated_residual", "w8a8_linear_gated_residual",
               "w8a8_layernorm_modulate_bf16", "w8a8_layernorm_modulate_quantize_act", "w8a8_quantize_v_fp8",
-              "w8a8_linear_gelu", "w8a8_linear_rmsnorm_modulate", "w8a8_linear_layernorm_modulate"):
+              "w8a8_linear_gelu", "w8a8_linear_rmsnorm_modulate", "w8a8_linear_layernorm_modulate",
+              "w8a8_linear_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

@@ -17,7 +17,7 @@ OUT = os.path.join(PKG, "libw8a8.so")
 
 SOURCES = ["w8a8_api.cpp", "quantize_block.hip", "quantize_rows.hip", "gemm_i8_blockscale.hip",
            "gemm_bf16.hip", "gelu_quantize.hip",
-           "qk_quantize.hip", "rmsnorm_quantize.hip", "gated_residual.hip"]
+           "qk_quantize.hip", "rmsnorm_quantize.hip", "gated_residual.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -9,14 +9,17 @@
 #include "w8a8_internal.h"
 
 namespace {
-
 thread_local int g_last_hip_error = 0;
+}  // namespace
 
-int hip_status(hipError_t e) {
-    if (e == hipSuccess) return W8A8_OK;
+int w8a8::hip_failure(hipError_t e) {
     g_last_hip_error = (int)e;
     return W8A8_ERR_HIP;
 }
+
+namespace {
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W8A8_OK : w8a8::hip_failure(e); }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -134,6 +137,17 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
 int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
                 const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
                 void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out) {
+    return w8a8::guarded_linear(x, x_dtype, M, K, N, w_bf16, qw, sw, bias_bf16, y_bf16, workspace, workspace_bytes,
+                                stream, path_out);
+}
+
+}  // extern "C"
+
+namespace w8a8 {
+
+int guarded_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16, const int8_t *qw,
+                   const float *sw, const void *bias_bf16, void *y_bf16, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream, int *path_out) {
     if (!x || !w_bf16 || !y_bf16 || M <= 0 || K <= 0 || N <= 0 || !valid_dtype(x_dtype))
         return W8A8_ERR_INVALID_ARG;
     if ((qw == nullptr) != (sw == nullptr)) return W8A8_ERR_INVALID_ARG;
@@ -160,6 +174,10 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, con
                                              static_cast<const uint16_t *>(bias_bf16), M, N, K,
                                              static_cast<uint16_t *>(y_bf16), stream));
 }
+
+}  // namespace w8a8
+
+extern "C" {
 
 // Two equally sized ranges that overlap without coinciding (exact aliasing
 // is the in-place case some entries allow).

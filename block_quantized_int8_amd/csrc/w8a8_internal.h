@@ -67,6 +67,16 @@ hipError_t launch_modulate_quantize(const uint16_t *x, const float *stats, bool 
 hipError_t launch_gemm_bf16_tiled(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M,
                                   int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
 
+// Records a failed HIP call in the per-thread slot of w8a8_last_hip_error
+// and returns W8A8_ERR_HIP.
+int hip_failure(hipError_t e);
+
+// The body of w8a8_linear (guard, checks, launches) with the caller's
+// workspace; shared by the entry points that bring the workspace differently.
+int guarded_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16, const int8_t *qw,
+                   const float *sw, const void *bias_bf16, void *y_bf16, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream, int *path_out);
+
 // x_dtype: 0 bf16, 1 fp16, 2 fp32 (the W8A8_DTYPE_* codes).
 hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,
                             int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);

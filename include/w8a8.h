@@ -133,6 +133,28 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, con
                 const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
                 void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out);
 
+/* Size of the device array that w8a8_linear_noalloc uses as its workspace:
+ * 32 MiB + 64 KiB, enough for M*K up to 2^25 (e.g. 8192 x 4096). */
+#define W8A8_NOALLOC_SCRATCH_BYTES (33554432 + 65536)
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): w8a8_linear with no
+ * workspace argument.  The INT8 path's qx and sx go to a fixed device array
+ * of W8A8_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends; this entry never allocates or frees memory.
+ * Same guard, arguments, results and errors as w8a8_linear, plus:
+ * W8A8_ERR_UNSUPPORTED when qw is given and w8a8_linear_workspace_bytes(M, K)
+ * exceeds the array (use w8a8_linear with a caller workspace then);
+ * W8A8_ERR_HIP if the array's device address cannot be obtained.  The array
+ * belongs to the stream's device (the current device for the null stream).
+ * Calls share it: calls that overlap in time on one GPU (several streams,
+ * several threads) race on its contents and must be ordered by the caller.
+ */
+int w8a8_linear_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16,
+                        const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16, hipStream_t stream,
+                        int *path_out);
+
 /*
  * The guard alone (host only, pure, touches no device): W8A8_PATH_INT8 iff
  * x_dtype is bf16, M, K and N are multiples of 128 and has_qweight != 0;
