@@ -52,7 +52,8 @@ __all__ = ["quantize_weight", "quantize_act", "gemm_blockscale", "linear", "rout
            "W8A8Error", "lib",
            "quantize_rows", "gemm_postscale", "linear_postscale", "postscale_workspace_bytes",
            "POSTSCALE_MAX_K", "gelu_bf16", "gelu_quantize_act", "quantize_qk",
-           "rmsnorm_modulate_bf16", "rmsnorm_modulate_quantize_act", "layernorm_modulate_bf16",
+           "rmsnorm_modulate_bf16", "rmsnorm_modulate_quantize_act", "rmsnorm_quantize_workspace_bytes",
+           "layernorm_modulate_bf16",
            "layernorm_modulate_quantize_act", "rope_bf16", "rope_quantize_qk", "quantize_v_fp8",
            "gated_residual", "gemm_blockscale_gated_residual", "linear_gelu", "linear_modulated",
            "producer_workspace_bytes", "force_fallback",
@@ -180,11 +181,16 @@ def rmsnorm_modulate_bf16(x: torch.Tensor, scale: torch.Tensor, shift: torch.Ten
     return out
 
 
+def rmsnorm_quantize_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().w8a8_rmsnorm_quantize_workspace_bytes(M, K))
+
+
 def rmsnorm_modulate_quantize_act(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6,
-                                  q=None, s=None):
+                                  q=None, s=None, workspace=None):
     """Block quantization of the modulated RMS normalization of x [B, L, K],
     fused (the bf16 result is never written) -> (q int8 [B*L, K],
-    s fp32 [B*L/128, K/128])."""
+    s fp32 [B*L/128, K/128]).  `workspace` (uint8, device, optional) is the
+    entry point's scratch memory, allocated here when not given."""
     x3, B, L, K = _modulation_args(x, scale, shift)
     M = B * L
     if q is None:
@@ -195,10 +201,14 @@ def rmsnorm_modulate_quantize_act(x: torch.Tensor, scale: torch.Tensor, shift: t
     _need_cuda("s", s, torch.float32)
     if q.numel() != M * K or s.numel() < (M // BLOCK) * (K // BLOCK):
         raise ValueError("output buffers have the wrong size")
-    r = torch.empty(M, dtype=torch.float32, device=x.device)       # the entry point's workspace
+    need = rmsnorm_quantize_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _need_cuda("workspace", workspace, torch.uint8)
     check("w8a8_rmsnorm_modulate_quantize_act",
           lib().w8a8_rmsnorm_modulate_quantize_act(_ptr(x3), B, L, K, _ptr(scale), _ptr(shift), float(eps),
-                                                   _ptr(r), _ptr(q), _ptr(s), _stream(x.device)))
+                                                   _ptr(workspace), workspace.numel(), _ptr(q), _ptr(s),
+                                                   _stream(x.device)))
     return q, s
 
 

@@ -29,6 +29,7 @@ EXPORTS = (
     "w8a8_linear_gated_residual", "w8a8_layernorm_modulate_bf16", "w8a8_layernorm_modulate_quantize_act",
     "w8a8_quantize_v_fp8", "w8a8_linear_producer_workspace_bytes", "w8a8_linear_gelu",
     "w8a8_linear_rmsnorm_modulate", "w8a8_linear_layernorm_modulate", "w8a8_linear_noalloc",
+    "w8a8_rmsnorm_quantize_workspace_bytes",
 )
 POSTSCALE_MAX_K = 133120
 BLOCK_MAX_K = 4194304
@@ -86,8 +87,10 @@ def lib():
     L.w8a8_layernorm_modulate_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P,
                                                        _P, _P]
     L.w8a8_rmsnorm_modulate_bf16.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P, _P]
-    L.w8a8_rmsnorm_modulate_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P, _P, _P,
-                                                     _P]
+    L.w8a8_rmsnorm_modulate_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_double, _P,
+                                                     ctypes.c_size_t, _P, _P, _P]
+    L.w8a8_rmsnorm_quantize_workspace_bytes.argtypes = [_I64, _I64]
+    L.w8a8_rmsnorm_quantize_workspace_bytes.restype = ctypes.c_size_t
     L.w8a8_linear_producer_workspace_bytes.argtypes = [_I64, _I64]
     L.w8a8_linear_producer_workspace_bytes.restype = ctypes.c_size_t
     L.w8a8_linear_gelu.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P,

@@ -25,14 +25,18 @@
 // over the row in ln_rows, from registers for the common widths; the
 // modulate kernels read (m, r) pairs).
 //
-// Three kernels: rms_rows (one wavefront per row, 16-byte loads, fp64
-// partial sums) writes r [B*L]; modulate_bf16 (one wavefront per row) writes
-// y; modulate_quantize (one workgroup per 128x128 block, the block
+// Kernels: rms_rows / ln_rows (one wavefront per row, 16-byte loads, fp64
+// partial sums) write r [B*L] / (m, r) pairs; modulate_bf16 (one wavefront per
+// row) writes y; modulate_quantize (one workgroup per 128x128 block, the block
 // quantizer's structure) computes y in registers and emits its codes and
-// scale, so the bf16 y never reaches HBM.  The fused pair reads x twice
-// (the second time with nontemporal loads: it is x's last use) and writes
-// one byte per element; the unfused chain reads it twice and also writes and
-// re-reads the bf16 y.
+// scale, so the bf16 y never reaches HBM.  That pair reads x twice (the second
+// time with nontemporal loads: it is x's last use) and writes one byte per
+// element.  rms_band_quantize (RMS form, K a multiple of 256) reads x once:
+// the workgroups of a 128-row band each hold a 256-column slice in
+// registers and exchange fp64 row partials through the workspace (its own
+// section below).  The layer form keeps the two-read pair: it would need two
+// exchanges (the mean, then the deviations), which cost more than the
+// second read saves.
 #include <math.h>
 
 #include "quant_math.h"
@@ -325,6 +329,253 @@ __global__ __launch_bounds__(kBlkThreads) void modulate_quantize_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Single-read RMS form of the fused producer (K a multiple of 256).
+//
+// One workgroup per item (128-row band, 256-column part): P = K / 256 items
+// per band, item = blockIdx.x, band = item / P.  The workgroup loads its
+// 128 x 256 slice of x once into registers (16 chunks of 8 bf16 per
+// thread), and
+//   1. sums the squares of its slice per row in fp64 (per thread and row,
+//      then the 16 chunk partials of a row in a fixed order through LDS) and
+//      stores the 128 row partials at partials[band][part][row] with
+//      device-coherent stores;
+//   2. waits for its stores, then adds 1 to the band's arrival counter and
+//      waits until the counter reaches P (all partials of the band visible);
+//   3. sums the P partials of each row in part order (every workgroup of the
+//      band does the same sum, so all see the same r), forms r, and
+//      modulates and quantizes its slice from registers as
+//      modulate_quantize_kernel does.
+// So x is read once; the exchange costs 8 bytes per row per part written and
+// P times that read (1/32 of x's bytes at P = 16).  The row sums are fp64 sums
+// of exact squares in this kernel's order (see the file header for the
+// effect of order).
+//
+// Progress: a workgroup waits only for the other items of its band, which
+// are the P consecutive workgroup ids around it.  Workgroups are dispatched
+// in id order, and an item of an older band never waits on a younger one, so
+// every older band completes and frees its slots; a band whose items are not
+// all resident can only be the youngest one dispatched, and it becomes whole
+// once the slots ahead of it free up.  The wait is still bounded: after
+// kSpinLimit polls the workgroup sets the workspace's error word and goes on
+// (its codes are then wrong), so no schedule can hang the device.
+//
+// Workspace (16-byte aligned): [0, 256) control (word 0: error word, 0 when
+// every wait completed), then one 256-byte line per band holding its
+// arrival counter (counters never share a cache line), then the fp64
+// partials [bands][P][128].  zero_counters_kernel clears the control word
+// and the counters before every launch (no memset, so the pair can be
+// captured in a graph and replayed).
+
+constexpr int kBandBlocks = kBandCols / kBlock;      // 128-column blocks per item: 2
+constexpr int kSpinLimit = 1 << 20;                  // polls before a wait gives up (~1 s)
+constexpr size_t kCtrlLine = kBandCtrlLine;          // bytes per counter line
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// (1 + scale) and shift of 8 consecutive columns, as fp32.
+struct ColMod {
+    float one_s[8], h[8];
+};
+
+__device__ __forceinline__ ColMod load_colmod(const uint16_t *scale, const uint16_t *shift) {
+    const u32x4 sc = *reinterpret_cast<const u32x4 *>(scale);
+    const u32x4 sh = *reinterpret_cast<const u32x4 *>(shift);
+    const uint32_t a[4] = {sc.x, sc.y, sc.z, sc.w}, b[4] = {sh.x, sh.y, sh.z, sh.w};
+    ColMod m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m.one_s[2 * i] = 1.0f + lo_bf16(a[i]);
+        m.one_s[2 * i + 1] = 1.0f + hi_bf16(a[i]);
+        m.h[2 * i] = lo_bf16(b[i]);
+        m.h[2 * i + 1] = hi_bf16(b[i]);
+    }
+    return m;
+}
+
+// y = bf16(((x * r) * (1 + s)) + h) for one chunk, each step one fp32 operation.
+__device__ __forceinline__ u32x4 rms_modulate_chunk(u32x4 x, const ColMod &md, float r) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float y0 = lo_bf16(w[i]) * r * md.one_s[2 * i] + md.h[2 * i];
+        const float y1 = hi_bf16(w[i]) * r * md.one_s[2 * i + 1] + md.h[2 * i + 1];
+        o[i] = bf16_bits(y0) | (bf16_bits(y1) << 16);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Running max of the 15-bit magnitudes of a chunk (packed 16-bit max).
+__device__ __forceinline__ u16x2 absmax_acc(u16x2 acc, u32x4 w) {
+    const u16x2 a = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu);
+    const u16x2 c = __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu);
+    return __builtin_elementwise_max(__builtin_elementwise_max(acc, __builtin_elementwise_max(a, b)),
+                                     __builtin_elementwise_max(c, d));
+}
+
+// Sum of squares of a chunk: each square of a bf16 value is exact in fp64,
+// so the fused multiply-add rounds exactly as the separate product and sum.
+__device__ __forceinline__ double sq_sum_chunk(u32x4 w) {
+    double a = 0.0;
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double l = (double)lo_bf16(v[i]), h = (double)hi_bf16(v[i]);
+        a = __builtin_fma(l, l, a);
+        a = __builtin_fma(h, h, a);
+    }
+    return a;
+}
+
+// Device-coherent loads through a buffer resource (cache policy sc1): plain
+// loads to the compiler, so many are in flight at once; offsets past
+// `bytes` read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__global__ void zero_counters_kernel(uint32_t *ctrl, int64_t lines) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < lines) ctrl[i * (kCtrlLine / 4)] = 0u;
+}
+
+__global__ __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void rms_band_quantize_kernel(
+    const uint16_t *__restrict__ x, int64_t K, uint32_t P, uint32_t L, double eps,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ shift, uint32_t *ctrl, double *partials,
+    int8_t *__restrict__ q, float *__restrict__ s) {
+    __shared__ double red64[kBlock][kChunksPerRow + 1];
+    __shared__ float s_r[kBlock];
+    __shared__ uint32_t red[kBlkThreads / 64][kBandBlocks];
+    const int t = threadIdx.x;
+    const int64_t item = blockIdx.x;
+    const int64_t band = item / P, part = item - band * P;
+    const int chunk = t % kChunksPerRow, r0 = t / kChunksPerRow;
+    const int64_t row0 = band * kBlock + r0;
+    const int64_t col0 = part * kBandCols + chunk * 8;
+    // uniform base of the slice + one 32-bit per-thread offset (r0 K + 8 chunk < 2^31: K < 2^26)
+    const uint32_t voff = (uint32_t)r0 * (uint32_t)K + (uint32_t)chunk * 8u;
+    const uint16_t *xb = x + band * kBlock * K + part * kBandCols;
+
+    u32x4 v[kBandBlocks][kPasses];
+#pragma unroll
+    for (int j = 0; j < kBandBlocks; ++j)
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p)
+            v[j][p] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(xb + (int64_t)kRowsPerPass * p * K + j * kBlock + voff));
+
+    // 1. row partials of this slice
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        double a = 0.0;
+#pragma unroll
+        for (int j = 0; j < kBandBlocks; ++j) {
+            a += sq_sum_chunk(v[j][p]);
+            asm volatile("" : "+v"(v[j][p]));  // the later pass unpacks again instead of keeping floats live
+        }
+        red64[r0 + kRowsPerPass * p][chunk] = a;
+    }
+    __syncthreads();
+    double *band_partials = partials + band * (int64_t)P * kBlock;
+    if (t < kBlock) {
+        double a = 0.0;
+#pragma unroll
+        for (int c = 0; c < kChunksPerRow; ++c) a += red64[t][c];
+        __hip_atomic_store(band_partials + part * kBlock + t, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // 2. arrive once the stores are complete; wait for the band
+    uint32_t *cnt = ctrl + (1 + band) * (kCtrlLine / 4);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0) {
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int spins = 0;
+        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < P) {
+            if (++spins > kSpinLimit) {
+                __hip_atomic_store(ctrl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+
+    // 3. r of the band's rows, then modulate + quantize from registers
+    if (t < kBlock) {
+        const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(band_partials, P * (uint32_t)kBlock * 8u);
+        double sum = 0.0;
+#pragma unroll 8
+        for (uint32_t pp = 0; pp < P; ++pp)
+            sum += __builtin_bit_cast(double,
+                                      __builtin_amdgcn_raw_buffer_load_b64(rs, (pp * kBlock + (uint32_t)t) * 8u, 0, 16));
+        s_r[t] = (float)(1.0 / sqrt(sum / (double)K + eps));
+    }
+    __syncthreads();
+
+    const uint32_t b_first = (uint32_t)(band * kBlock) / L, b_last = (uint32_t)(band * kBlock + kBlock - 1) / L;
+#pragma unroll
+    for (int j = 0; j < kBandBlocks; ++j) {
+        u16x2 mx = u16x2{0, 0};
+        if (b_first == b_last) {
+            const ColMod md = load_colmod(scale + (int64_t)b_first * K + col0 + j * kBlock,
+                                          shift + (int64_t)b_first * K + col0 + j * kBlock);
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                v[j][p] = rms_modulate_chunk(v[j][p], md, s_r[r0 + kRowsPerPass * p]);
+                mx = absmax_acc(mx, v[j][p]);
+                __builtin_amdgcn_sched_barrier(0);  // one row at a time keeps the register count down
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                const uint32_t b = (uint32_t)(row0 + kRowsPerPass * p) / L;
+                const ColMod md =
+                    load_colmod(scale + (int64_t)b * K + col0 + j * kBlock, shift + (int64_t)b * K + col0 + j * kBlock);
+                v[j][p] = rms_modulate_chunk(v[j][p], md, s_r[r0 + kRowsPerPass * p]);
+                mx = absmax_acc(mx, v[j][p]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        uint32_t m = max((uint32_t)mx.x, (uint32_t)mx.y);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+        if ((t & 63) == 0) red[t >> 6][j] = m;
+    }
+    __syncthreads();
+    const int64_t col_blocks = K / kBlock;
+#pragma unroll
+    for (int j = 0; j < kBandBlocks; ++j) {
+        const uint32_t m = max(max(red[0][j], red[1][j]), max(red[2][j], red[3][j]));
+        const float a = __uint_as_float(m << 16);
+        const float sc = a / 127.0f;  // IEEE division, correctly rounded
+        if (t == 0) s[band * col_blocks + part * kBandBlocks + j] = sc;
+        int8_t *qb = q + band * kBlock * K + part * kBandCols + j * kBlock;
+        if (m == 0) {
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p)
+                *reinterpret_cast<u32x2 *>(qb + (int64_t)p * kRowsPerPass * K + voff) = u32x2{0u, 0u};
+        } else if (sc < kTinyScale) {
+            const float f = kPrescale, ss = sc * f, rcp = 1.0f / ss;
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                *reinterpret_cast<u32x2 *>(qb + (int64_t)p * kRowsPerPass * K + voff) = code_chunk<true>(v[j][p], f, ss, rcp);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            const float rcp = 1.0f / sc;
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                *reinterpret_cast<u32x2 *>(qb + (int64_t)p * kRowsPerPass * K + voff) =
+                    code_chunk<false>(v[j][p], 1.0f, sc, rcp);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_rms_rows(const uint16_t *x, int64_t rows, int64_t K, double eps, float *r, hipStream_t stream) {
@@ -381,6 +632,25 @@ hipError_t launch_modulate_quantize(const uint16_t *x, const float *stats, bool 
     else
         modulate_quantize_kernel<false><<<dim3((unsigned)tiles), dim3(kBlkThreads), 0, stream>>>(
             x, stats, (uint32_t)L, K, col_blocks, scale, shift, q, s);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_rms_band_quantize(const uint16_t *x, int64_t rows, int64_t L, int64_t K, double eps,
+                                    const uint16_t *scale, const uint16_t *shift, void *workspace, int8_t *q,
+                                    float *s, hipStream_t stream) {
+    const int64_t bands = rows / kBlock, P = K / kBandCols;
+    const int64_t items = bands * P;
+    if (items <= 0) return hipSuccess;
+    if (items > 0x7FFFFFFF || rows > 0x7FFFFFFF || L > 0x7FFFFFFF || K >= (int64_t)1 << 26) return hipErrorInvalidValue;
+    uint32_t *ctrl = static_cast<uint32_t *>(workspace);
+    double *partials = reinterpret_cast<double *>(static_cast<char *>(workspace) + kCtrlLine * (size_t)(1 + bands));
+    const int64_t lines = 1 + bands;
+    zero_counters_kernel<<<dim3((unsigned)((lines + 255) / 256)), dim3(256), 0, stream>>>(ctrl, lines);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    rms_band_quantize_kernel<<<dim3((unsigned)items), dim3(kBlkThreads), 0, stream>>>(
+        x, K, (uint32_t)P, (uint32_t)L, eps, scale, shift, ctrl, partials, q, s);
     return hipGetLastError();
 }
 

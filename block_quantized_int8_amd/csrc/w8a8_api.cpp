@@ -437,22 +437,46 @@ int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t
                                                  static_cast<uint16_t *>(y_bf16), stream));
 }
 
+// Bytes of the control line (word 0: the wait error word) that starts the
+// workspace of the fused RMS producer.
+static constexpr size_t kRmsCtrl = 256;
+
+// The fused RMS producer reads x once (the band kernel) when K % 256 == 0,
+// else runs the row-statistics kernel and the two-read quantizer, with r
+// after the control line.
+static bool rms_single_read(int64_t K) { return K % 256 == 0 && K < ((int64_t)1 << 26); }
+
+size_t w8a8_rmsnorm_quantize_workspace_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    if (rms_single_read(K)) return round256(w8a8::rms_band_workspace_bytes(M, K));
+    return kRmsCtrl + round256((size_t)M * sizeof(float));
+}
+
+// Fused RMS producer into qx/sx with `ws` (device, 16-byte aligned, large enough).
+static hipError_t rms_quantize(const uint16_t *x, int64_t M, int64_t L, int64_t K, double eps, const uint16_t *scale,
+                               const uint16_t *shift, void *ws, int8_t *qx, float *sx, hipStream_t stream) {
+    if (rms_single_read(K)) return w8a8::launch_rms_band_quantize(x, M, L, K, eps, scale, shift, ws, qx, sx, stream);
+    float *r = reinterpret_cast<float *>(static_cast<char *>(ws) + kRmsCtrl);
+    const hipError_t e = w8a8::launch_rms_rows(x, M, K, eps, r, stream);
+    if (e != hipSuccess) return e;
+    return w8a8::launch_modulate_quantize(x, r, false, M, L, K, scale, shift, qx, sx, stream);
+}
+
 int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
-                                       const void *shift_bf16, double eps, float *r_ws, int8_t *qx, float *sx,
-                                       hipStream_t stream) {
-    const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, r_ws);
+                                       const void *shift_bf16, double eps, void *workspace, size_t workspace_bytes,
+                                       int8_t *qx, float *sx, hipStream_t stream) {
+    const int st = rmsnorm_args(x_bf16, B, L, K, scale_bf16, shift_bf16, eps, static_cast<const float *>(workspace));
     if (st != W8A8_OK) return st;
     if (!qx || !sx) return W8A8_ERR_INVALID_ARG;
-    if (!mult128(B * L) || !mult128(K) || !aligned(qx, 16) || !aligned(sx, 4)) return W8A8_ERR_UNSUPPORTED;
-    if (!is_device_ptr(x_bf16) || !is_device_ptr(scale_bf16) || !is_device_ptr(shift_bf16) || !is_device_ptr(r_ws) ||
-        !is_device_ptr(qx) || !is_device_ptr(sx))
+    if (!mult128(B * L) || !mult128(K) || !aligned(qx, 16) || !aligned(sx, 4) || !aligned(workspace, 16))
+        return W8A8_ERR_UNSUPPORTED;
+    if (workspace_bytes < w8a8_rmsnorm_quantize_workspace_bytes(B * L, K)) return W8A8_ERR_INVALID_ARG;
+    if (!is_device_ptr(x_bf16) || !is_device_ptr(scale_bf16) || !is_device_ptr(shift_bf16) ||
+        !is_device_ptr(workspace) || !is_device_ptr(qx) || !is_device_ptr(sx))
         return W8A8_ERR_INVALID_ARG;
-    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
-    hipError_t e = w8a8::launch_rms_rows(x, B * L, K, eps, r_ws, stream);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(w8a8::launch_modulate_quantize(x, r_ws, false, B * L, L, K,
-                                                     static_cast<const uint16_t *>(scale_bf16),
-                                                     static_cast<const uint16_t *>(shift_bf16), qx, sx, stream));
+    return hip_status(rms_quantize(static_cast<const uint16_t *>(x_bf16), B * L, L, K, eps,
+                                   static_cast<const uint16_t *>(scale_bf16),
+                                   static_cast<const uint16_t *>(shift_bf16), workspace, qx, sx, stream));
 }
 
 int w8a8_layernorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
@@ -496,14 +520,16 @@ int w8a8_layernorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t 
 size_t w8a8_linear_producer_workspace_bytes(int64_t M, int64_t K) {
     if (M <= 0 || K <= 0) return 0;
     const size_t stats = round256((size_t)M * 2 * sizeof(float));
+    const size_t rms = w8a8_rmsnorm_quantize_workspace_bytes(M, K);
     const size_t fallback = round256((size_t)M * (size_t)K * 2) + stats;
-    const size_t int8 = w8a8_linear_workspace_bytes(M, K) + stats;
+    const size_t int8 = w8a8_linear_workspace_bytes(M, K) + (rms > stats ? rms : stats);
     return fallback > int8 ? fallback : int8;
 }
 
 // Workspace of the producer linears: on the INT8 path qx and sx (as in
-// w8a8_linear) then the per-row statistics; on the fallback the producer's
-// bf16 output [M, K] then the statistics.
+// w8a8_linear) then the per-row statistics (for the RMS form, the fused
+// producer's whole workspace); on the fallback the producer's bf16 output
+// [M, K] then the statistics.
 static float *producer_stats(void *workspace, int path, int64_t M, int64_t K) {
     const size_t off = path == W8A8_PATH_INT8 ? w8a8_linear_workspace_bytes(M, K) : round256((size_t)M * (size_t)K * 2);
     return reinterpret_cast<float *>(static_cast<char *>(workspace) + off);
@@ -566,16 +592,21 @@ static int linear_modulated(bool layer, const void *x_bf16, int64_t B, int64_t L
     const uint16_t *bias = static_cast<const uint16_t *>(bias_bf16);
     uint16_t *y = static_cast<uint16_t *>(y_bf16);
     float *stats = producer_stats(workspace, path, M, K);
-    hipError_t e = layer ? w8a8::launch_ln_rows(x, M, K, eps, stats, stream)
-                         : w8a8::launch_rms_rows(x, M, K, eps, stats, stream);
-    if (e != hipSuccess) return hip_status(e);
+    hipError_t e;
     if (path == W8A8_PATH_INT8) {
         int8_t *qx = static_cast<int8_t *>(workspace);
         float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) + round256((size_t)M * (size_t)K));
-        e = w8a8::launch_modulate_quantize(x, stats, layer, M, L, K, scale, shift, qx, sx, stream);
+        if (layer) {
+            e = w8a8::launch_ln_rows(x, M, K, eps, stats, stream);
+            if (e == hipSuccess) e = w8a8::launch_modulate_quantize(x, stats, true, M, L, K, scale, shift, qx, sx, stream);
+        } else {
+            e = rms_quantize(x, M, L, K, eps, scale, shift, stats, qx, sx, stream);
+        }
         if (e != hipSuccess) return hip_status(e);
         return hip_status(w8a8::launch_gemm_i8_blockscale(qx, sx, qw, sw, bias, M, N, K, y, stream));
     }
+    e = layer ? w8a8::launch_ln_rows(x, M, K, eps, stats, stream) : w8a8::launch_rms_rows(x, M, K, eps, stats, stream);
+    if (e != hipSuccess) return hip_status(e);
     uint16_t *g = static_cast<uint16_t *>(workspace);
     e = w8a8::launch_modulate_bf16(x, stats, layer, M, L, K, scale, shift, g, stream);
     if (e != hipSuccess) return hip_status(e);

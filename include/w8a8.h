@@ -265,16 +265,21 @@ int w8a8_gelu_quantize_act(const void *y_bf16, int64_t M, int64_t K, int8_t *qx,
  * each fl32 one IEEE fp32 operation, bf16 rounding to nearest even.  The sum
  * of squares is an fp64 sum in the kernel's order; another order can move
  * it by a few fp64 ulps, which changes r only when r lies within ~2^-50 of
- * an fp32 rounding boundary.  r_ws is a caller-provided workspace of B*L
- * floats that receives r.  eps must be finite and > 0, inputs finite;
+ * an fp32 rounding boundary.  eps must be finite and > 0, inputs finite;
  * B*L < 2^31.  Errors: null pointers, sizes <= 0 or a bad eps ->
- * W8A8_ERR_INVALID_ARG; K % 8 != 0, x, scale, shift (and y or qx) not
- * 16-byte aligned or r_ws not 4-byte aligned -> W8A8_ERR_UNSUPPORTED.
+ * W8A8_ERR_INVALID_ARG; K % 8 != 0 or x, scale, shift (and y or qx) not
+ * 16-byte aligned -> W8A8_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 
-/* y_bf16 [B*L, K] = the modulated normalization of x (any B*L >= 1). */
+/* y_bf16 [B*L, K] = the modulated normalization of x (any B*L >= 1); r_ws is
+ * a caller-provided workspace of B*L floats (4-byte aligned, else
+ * W8A8_ERR_UNSUPPORTED) that receives r. */
 int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
                                const void *shift_bf16, double eps, float *r_ws, void *y_bf16, hipStream_t stream);
+
+/* Bytes of workspace w8a8_rmsnorm_modulate_quantize_act needs for M = B*L
+ * rows of width K (0 when M or K <= 0). */
+size_t w8a8_rmsnorm_quantize_workspace_bytes(int64_t M, int64_t K);
 
 /*
  * Fused producer + quantize: y as above, quantized by the block rule of
@@ -282,10 +287,22 @@ int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t
  * without ever being written (equal, bit for bit, to w8a8_quantize_act
  * applied to w8a8_rmsnorm_modulate_bf16's output).  B*L and K must be
  * multiples of 128 (else W8A8_ERR_UNSUPPORTED).
+ *
+ * When K % 256 == 0, x is read once: the workgroups of each 128-row band
+ * hold 256-column slices in registers and exchange fp64 row partials through
+ * the workspace, waiting for one another (bounded: a wait that does not
+ * complete in ~1 s gives up and leaves the codes of its slice wrong; the
+ * workspace's first 32-bit word is cleared at the start of such a call and
+ * set nonzero by a wait that gives up).  Other widths take two reads of x
+ * and do not touch that word.  workspace: device memory,
+ * 16-byte aligned (else W8A8_ERR_UNSUPPORTED), at least
+ * w8a8_rmsnorm_quantize_workspace_bytes(B*L, K) bytes (else
+ * W8A8_ERR_INVALID_ARG); its contents on return are scratch apart from that
+ * first word.  Calls that share a workspace must not overlap in time.
  */
 int w8a8_rmsnorm_modulate_quantize_act(const void *x_bf16, int64_t B, int64_t L, int64_t K, const void *scale_bf16,
-                                       const void *shift_bf16, double eps, float *r_ws, int8_t *qx, float *sx,
-                                       hipStream_t stream);
+                                       const void *shift_bf16, double eps, void *workspace, size_t workspace_bytes,
+                                       int8_t *qx, float *sx, hipStream_t stream);
 
 /*
  * The layer-normalization form of the producer (the fused-kernels paragraph

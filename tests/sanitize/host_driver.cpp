@@ -51,6 +51,10 @@ hipError_t launch_modulate_quantize(const uint16_t *, const float *, bool, int64
 hipError_t launch_quantize_v_fp8(const uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t, uint8_t *, float *,
                                  hipStream_t) { reached("quantize_v_fp8"); }
 hipError_t launch_ln_rows(const uint16_t *, int64_t, int64_t, double, float *, hipStream_t) { reached("ln_rows"); }
+hipError_t launch_rms_band_quantize(const uint16_t *, int64_t, int64_t, int64_t, double, const uint16_t *,
+                                    const uint16_t *, void *, int8_t *, float *, hipStream_t) {
+    reached("rms_band_quantize");
+}
 }  // namespace w8a8
 
 #define CHECK(cond)                                                                    \
@@ -176,9 +180,17 @@ int main() {
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 2, 64, 256, static_cast<char *>(p) + 8, p, 1e-6, f, p, nullptr) ==
           W8A8_ERR_UNSUPPORTED);
     CHECK(w8a8_rmsnorm_modulate_bf16(p, 1LL << 20, 1LL << 12, 256, p, p, 1e-6, f, p, nullptr) == W8A8_ERR_UNSUPPORTED);
-    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 100, 256, p, p, 1e-6, f, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
-    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 200, p, p, 1e-6, f, q8, f, nullptr) == W8A8_ERR_UNSUPPORTED);
-    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 256, p, p, 1e-6, f, nullptr, f, nullptr) ==
+    const size_t rws = w8a8_rmsnorm_quantize_workspace_bytes(256, 256);
+    CHECK(rws == 256 * 3 + 256 * 8 && w8a8_rmsnorm_quantize_workspace_bytes(-1, 256) == 0);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 100, 256, p, p, 1e-6, p, rws, q8, f, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 200, p, p, 1e-6, p, rws, q8, f, nullptr) ==
+          W8A8_ERR_UNSUPPORTED);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 256, p, p, 1e-6, p, rws, nullptr, f, nullptr) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 256, p, p, 1e-6, p, rws - 1, q8, f, nullptr) ==
+          W8A8_ERR_INVALID_ARG);
+    CHECK(w8a8_rmsnorm_modulate_quantize_act(p, 2, 128, 256, p, p, 1e-6, nullptr, rws, q8, f, nullptr) ==
           W8A8_ERR_INVALID_ARG);
     // the path is decided before the workspace: a misaligned x takes the fallback, so a missing
     // workspace is not an error there (the call stops at the host-pointer check instead)

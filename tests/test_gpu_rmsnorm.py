@@ -55,9 +55,11 @@ def test_extreme_magnitudes_and_zero_rows():
     assert np.array_equal(gpu_y(x, L, sc, sh, 1e-6)[2], sh[0])
 
 
-@pytest.mark.parametrize("B,L,K", [(2, 384, 512), (4, 96, 256), (1, 128, 128)])
+@pytest.mark.parametrize("B,L,K", [(2, 384, 512), (4, 96, 256), (1, 128, 128), (4, 96, 1024), (2, 192, 2560),
+                                   (1, 256, 384)])
 def test_fused_codes_bit_exact(B, L, K):
-    # (4, 96): every second 128-row block holds rows of two batch entries
+    # L = 96, 192: some 128-row blocks hold rows of two batch entries; K % 256 == 0
+    # takes the single-read kernel (1 to 10 workgroups per band), K = 128, 384 the two-read pair
     x = random_bf16(B * 7 + L, (B * L, K), 2.0)
     sc = random_bf16(K + 3, (B, K), 0.3)
     sh = random_bf16(K + 4, (B, K), 0.3)
@@ -66,6 +68,25 @@ def test_fused_codes_bit_exact(B, L, K):
     oq, os_ = oracle.rmsnorm_modulate_quantize_block(x, L, sc, sh, 1e-6)
     assert np.array_equal(q.cpu().numpy(), oq)
     assert np.array_equal(s.cpu().numpy(), os_)
+
+
+def test_single_read_workspace_reuse_and_error_word():
+    """One workspace through calls of different widths: the single-read kernel
+    (K % 256 == 0) clears its counters itself on every call, so stale
+    counters of an earlier, larger call do not release a band early; its error
+    word stays 0; each result equals the unfused chain bit for bit."""
+    ws = torch.empty(w8a8.rmsnorm_quantize_workspace_bytes(1024, 4096), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)                       # nonzero garbage in the counters and partials
+    for i, (B, L, K) in enumerate([(2, 512, 4096), (2, 512, 4096), (3, 128, 768), (1, 256, 384), (4, 256, 2048)]):
+        x = dev(random_bf16(600 + i, (B * L, K), 2.0)).view(B, L, K)
+        sc, sh = dev(random_bf16(610 + i, (B, K), 0.3)), dev(random_bf16(620 + i, (B, K), 0.3))
+        q, s = w8a8.rmsnorm_modulate_quantize_act(x, sc, sh, 1e-6, workspace=ws)
+        q2, s2 = w8a8.quantize_act(w8a8.rmsnorm_modulate_bf16(x, sc, sh, 1e-6).view(B * L, K))
+        torch.cuda.synchronize()
+        assert torch.equal(q, q2) and torch.equal(s, s2), (B, L, K)
+        if K % 256 == 0:
+            assert int(ws[:4].view(torch.int32).item()) == 0, (B, L, K)
+        print(f"rms single-read reuse {B}x{L}x{K}: equal to the unfused chain", flush=True)
 
 
 def test_zero_modulated_block_gives_zero_scale():

@@ -139,11 +139,33 @@ def test_host_decided_errors_rmsnorm(L):
     assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 0, 256, fake, fake, 1e-6, fake, fake, null) == 1
     assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 64, 252, fake, fake, 1e-6, fake, fake, null) == 2
     assert L.w8a8_rmsnorm_modulate_bf16(fake, 2, 64, 256, fake, fake, 1e-6, null, fake, null) == 1
-    # fused: B*L and K multiples of 128
-    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 100, 256, fake, fake, 1e-6, fake, fake, fake, null) == 2
-    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 128, 192, fake, fake, 1e-6, fake, fake, fake, null) == 2
-    assert L.w8a8_rmsnorm_modulate_quantize_act(ctypes.c_void_p(0x1008), 2, 128, 256, fake, fake, 1e-6, fake, fake,
-                                                fake, null) == 2
+    # fused: B*L and K multiples of 128, a 16-byte aligned workspace of the stated size
+    big = 1 << 30
+    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 100, 256, fake, fake, 1e-6, fake, big, fake, fake,
+                                                null) == 2
+    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 128, 192, fake, fake, 1e-6, fake, big, fake, fake,
+                                                null) == 2
+    assert L.w8a8_rmsnorm_modulate_quantize_act(ctypes.c_void_p(0x1008), 2, 128, 256, fake, fake, 1e-6, fake, big,
+                                                fake, fake, null) == 2
+    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 128, 256, fake, fake, 1e-6, ctypes.c_void_p(0x1008), big,
+                                                fake, fake, null) == 2
+    need = L.w8a8_rmsnorm_quantize_workspace_bytes(256, 256)
+    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 128, 256, fake, fake, 1e-6, fake, need - 1, fake, fake,
+                                                null) == 1
+    assert L.w8a8_rmsnorm_modulate_quantize_act(fake, 2, 128, 256, fake, fake, 1e-6, null, big, fake, fake,
+                                                null) == 1
+
+
+def test_rmsnorm_quantize_workspace_bytes(L):
+    """Single-read widths (K % 256 == 0): a 256-byte control line, one 256-byte
+    counter line per 128-row band and 8 bytes per row per 256 columns; other
+    widths: the control line and 4 bytes of r per row."""
+    f = L.w8a8_rmsnorm_quantize_workspace_bytes
+    assert f(0, 256) == 0 and f(256, 0) == 0
+    assert f(32768, 4096) == 256 * (1 + 256) + 32768 * 16 * 8
+    assert f(256, 256) == 256 * 3 + 256 * 8
+    assert f(256, 384) == 256 + 1024
+    assert f(128, 128) == 256 + 512
 
 
 def test_host_decided_errors_rope(L):
