@@ -552,7 +552,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--only", choices=["gemm", "quantize", "linear", "gelu_quant", "gelu", "qk", "v", "rope", "rms",
-                                       "ln", "residual", "mlp_up", "mlp_down"],
+                                       "ln", "residual", "mlp_up", "mlp_down", "fallback"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -586,6 +586,22 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy calibration: {args.steps} copies of {n} bytes")
+        return
+
+    if args.only == "fallback":
+        # the guard's bf16 fallback on M = 4000 at 4096^2, then the BLAS
+        # library's bf16 linear on the same operands (for counter comparisons)
+        xf = gpu_normal(torch.Generator(device=dev).manual_seed(70), (4000, 4096), dev=dev)
+        wf = gpu_normal(torch.Generator(device=dev).manual_seed(71), (4096, 4096), 0.02, dev=dev)
+        lf = w8a8.W8A8Linear(wf)
+        for _ in range(args.steps):
+            lf(xf)
+        torch.cuda.synchronize()
+        assert lf.last_path == w8a8.PATH_BF16
+        for _ in range(args.steps):
+            torch.nn.functional.linear(xf, wf)
+        torch.cuda.synchronize()
+        log(f"--only fallback: {args.steps} launches of each done")
         return
 
     if args.only in ("mlp_up", "mlp_down"):
