@@ -32,8 +32,10 @@ vs three; and the INT8 quantization of a video self-attention's Q and K.
 the rotary embedding fused into the Q/K quantizer, the gated residual update
 in the GEMM epilogue and one transformer block's W8A8 work.
 
-Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|v|rope|rms|ln|residual|mlp_up|mlp_down
-launches just that work for --steps iterations (no oracle);
+Modes for profiling runs: --only gemm|quantize|linear|gelu_quant|gelu|qk|v|rope|rms|ln|residual|mlp_up|mlp_down|fallback
+launches just that work for --steps iterations (no oracle; fallback runs the
+guarded bf16 linear on the M = 4000 guard case, then the BLAS library's bf16
+linear on the same operands);
 --copy-calibration runs a plain 1 GiB device copy used to scale the HBM byte
 counters.
 """
