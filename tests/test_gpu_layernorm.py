@@ -68,9 +68,34 @@ def test_extreme_magnitudes_and_constant_rows():
     assert np.array_equal(y[2], sh[0]) and np.array_equal(y[3], sh[0])
 
 
-@pytest.mark.parametrize("B,L,K", [(2, 384, 512), (4, 96, 256), (1, 128, 128)])
+def test_fused_extreme_rows():
+    """The fused entry on rows that stress the statistics: tiny and huge
+    magnitudes, zero and constant rows, a few huge values, a mean far above
+    the spread, and halves of a row with different means (K = 1024)."""
+    B, L, K = 1, 128, 1024
+    xf = bf16_bits_to_f32(random_bf16(35, (B * L, K)))
+    xf[0] *= np.float32(2.0 ** -100)
+    xf[1] *= np.float32(2.0 ** 100)
+    xf[2] = 0.0
+    xf[3] = 7.0
+    xf[9, :5] = np.float32(1e30)
+    xf[10] += np.float32(1e4)
+    xf[11, 512:] += np.float32(300.0)
+    x = f32_to_bf16_bits(xf)
+    sc = random_bf16(36, (B, K), 0.3)
+    sh = random_bf16(37, (B, K), 0.3)
+    for eps in (1e-6, 1e-30):
+        q, s = w8a8.layernorm_modulate_quantize_act(dev(x).view(B, L, K), dev(sc), dev(sh), eps)
+        torch.cuda.synchronize()
+        oq, os_ = oracle.layernorm_modulate_quantize_block(x, L, sc, sh, eps)
+        assert np.array_equal(q.cpu().numpy(), oq), eps
+        assert np.array_equal(s.cpu().numpy(), os_), eps
+
+
+@pytest.mark.parametrize("B,L,K", [(2, 384, 512), (4, 96, 256), (1, 128, 128), (4, 96, 1024), (2, 192, 2560),
+                                   (1, 256, 384)])
 def test_fused_codes_bit_exact(B, L, K):
-    # (4, 96): every second 128-row block holds rows of two batch entries
+    # L = 96, 192: some 128-row blocks hold rows of two batch entries
     x = off_centre(B * 7 + L, B * L, K)
     sc = random_bf16(K + 3, (B, K), 0.3)
     sh = random_bf16(K + 4, (B, K), 0.3)
