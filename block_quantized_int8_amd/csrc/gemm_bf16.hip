@@ -44,6 +44,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
     return __builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> one word of two bf16 (lo first), one packed conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 template <int kDtype>
 __device__ __forceinline__ uint16_t load_as_bf16(const void *p, int64_t idx) {
     if constexpr (kDtype == 0) {
@@ -321,8 +329,8 @@ __global__ __launch_bounds__(kPThreads) void gemm_bf16_pipe_kernel(const uint16_
                 if (bias) v[e] += __uint_as_float((uint32_t)bias[n + e] << 16);
             }
             u32x2 out;
-            out.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-            out.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+            out.x = pack_bf16x2(v[0], v[1]);
+            out.y = pack_bf16x2(v[2], v[3]);
             *reinterpret_cast<u32x2 *>(y + m * N + n) = out;
         }
 }

@@ -87,6 +87,8 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // buffer descriptor word 3 for raw (untyped) dword buffer access on gfx9 parts
@@ -98,9 +100,10 @@ constexpr int kRsrcWord3 = 0x00020000;
 // read one chunk column without bank conflicts.  Self-inverse in `chunk`.
 __device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 
+// Two floats -> one word of two bf16 (lo first), each rounded to nearest
+// even: one packed conversion.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -54,8 +54,13 @@ constexpr int kPasses = kBlock / kRowsPerPass;      // 8
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ uint32_t bf16_bits(float v) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> one word of two bf16 (lo first), each rounded to nearest
+// even: one packed conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // kCenter: the layer normalization's (x - m) * r; else the RMS form x * r.
@@ -73,7 +78,7 @@ template <bool kCenter>
 __device__ __forceinline__ uint32_t modulate_word(uint32_t xw, uint32_t sw, uint32_t hw, float m, float r) {
     const float y0 = modulate<kCenter>(lo_bf16(xw), m, r, lo_bf16(sw), lo_bf16(hw));
     const float y1 = modulate<kCenter>(hi_bf16(xw), m, r, hi_bf16(sw), hi_bf16(hw));
-    return bf16_bits(y0) | (bf16_bits(y1) << 16);
+    return pack_bf16x2(y0, y1);
 }
 
 template <bool kCenter>
@@ -402,7 +407,7 @@ __device__ __forceinline__ u32x4 rms_modulate_chunk(u32x4 x, const ColMod &md, f
     for (int i = 0; i < 4; ++i) {
         const float y0 = lo_bf16(w[i]) * r * md.one_s[2 * i] + md.h[2 * i];
         const float y1 = hi_bf16(w[i]) * r * md.one_s[2 * i + 1] + md.h[2 * i + 1];
-        o[i] = bf16_bits(y0) | (bf16_bits(y1) << 16);
+        o[i] = pack_bf16x2(y0, y1);
     }
     return u32x4{o[0], o[1], o[2], o[3]};
 }
