@@ -59,8 +59,11 @@ def _gemm_case(M, N, K, seed, bias=False):
     return assert_bf16_close(bf16_bits(y), yo, f"gemm {M}x{N}x{K}")
 
 
+# K = 128: a single K-block, so every sub-tile's dequantization is the one
+# carried out of the main loop (the degenerate case of the pipeline)
 @pytest.mark.parametrize("M,N,K,bias", [(256, 256, 256, False), (384, 640, 512, True),
-                                        (1024, 256, 1024, False), (128, 1152, 384, True)])
+                                        (1024, 256, 1024, False), (128, 1152, 384, True),
+                                        (128, 128, 128, False), (384, 384, 128, True)])
 def test_gemm_vs_oracle(M, N, K, bias):
     _gemm_case(M, N, K, M * 7 + N, bias)
 

@@ -54,7 +54,8 @@ def test_quantize_rows_golden_and_floor():
 
 
 @pytest.mark.parametrize("M,N,K,bias", [(256, 256, 256, False), (384, 640, 512, True),
-                                        (128, 1152, 4096, True), (256, 256, 16384, False)])
+                                        (128, 1152, 4096, True), (256, 256, 16384, False),
+                                        (384, 384, 128, True)])
 def test_gemm_postscale(M, N, K, bias):
     x = random_bf16(M + K, (M, K))
     w = random_bf16(N + K, (N, K), 0.02)
