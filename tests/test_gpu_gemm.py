@@ -94,3 +94,23 @@ def test_block_gemm_long_k_scale_reload():
     y = w8a8.gemm_blockscale(_dev(qx), _dev(sx), _dev(qw), _dev(sw))
     torch.cuda.synchronize()
     assert_bf16_close(bf16_bits(y), oracle.linear_int8(qx, sx, qw, sw), "block GEMM K=65536")
+
+
+def test_block_gemm_at_max_k():
+    # K = 2^22, the largest K the block kernel accepts: 32768 K-blocks (the
+    # per-lane scale preload refilled 512 times) and operand byte offsets up
+    # to 255 * K inside a full 256 x 256 tile; output rows sampled
+    M = N = 256
+    K = w8a8.BLOCK_MAX_K
+    kbs = K // 128
+    rng = np.random.default_rng(4242)
+    qx = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    # scales spread over a few binades and different in every K-block, so a
+    # stale, shifted or transposed scale shows in the result
+    sx = (rng.uniform(0.5, 1.0, (M // 128, kbs)) * 2.0 ** -rng.integers(4, 12, (M // 128, kbs))).astype(np.float32)
+    sw = (rng.uniform(0.5, 1.0, (N // 128, kbs)) * 2.0 ** -rng.integers(4, 12, (N // 128, kbs))).astype(np.float32)
+    y = w8a8.gemm_blockscale(_dev(qx), _dev(sx), _dev(qw), _dev(sw))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 127, 128, 191, 200, 255])
+    assert_bf16_close(bf16_bits(y)[rows], oracle.linear_int8(qx, sx, qw, sw, rows=rows), "block GEMM at the K limit")
