@@ -39,6 +39,8 @@
 // second read saves.
 #include <math.h>
 
+#include <atomic>
+
 #include "quant_math.h"
 #include "w8a8_internal.h"
 
@@ -640,6 +642,36 @@ hipError_t launch_modulate_quantize(const uint16_t *x, const float *stats, bool 
     return hipGetLastError();
 }
 
+
+// The band's K / 256 workgroups wait for one another, so a band can only
+// complete once all of them are resident; a band larger than the device holds
+// at once would end only through the bounded wait (error word set, codes
+// wrong).  The single-read form is therefore taken only when a band needs at
+// most half of the device's resident capacity for this kernel (its occupancy
+// per CU times the CU count, queried once per device), which leaves room for
+// other work on the device or a CU mask.  A failed query answers false.
+bool rms_band_fits(int64_t K) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> capacity[kMaxDevices];  // 0: not queried yet, -1: none
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return false;
+    }
+    int cap = capacity[dev].load(std::memory_order_relaxed);
+    if (cap == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rms_band_quantize_kernel, kBlkThreads, 0) !=
+                hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        cap = cus > 0 && per_cu > 0 ? cus * per_cu : -1;
+        capacity[dev].store(cap, std::memory_order_relaxed);
+    }
+    return K > 0 && K / kBandCols <= cap / 2;
+}
 
 hipError_t launch_rms_band_quantize(const uint16_t *x, int64_t rows, int64_t L, int64_t K, double eps,
                                     const uint16_t *scale, const uint16_t *shift, void *workspace, int8_t *q,

@@ -441,9 +441,11 @@ int w8a8_rmsnorm_modulate_bf16(const void *x_bf16, int64_t B, int64_t L, int64_t
 // workspace of the fused RMS producer.
 static constexpr size_t kRmsCtrl = 256;
 
-// The fused RMS producer reads x once (the band kernel) when K % 256 == 0,
-// else runs the row-statistics kernel and the two-read quantizer, with r
-// after the control line.
+// The fused RMS producer can read x once (the band kernel) when K % 256 == 0;
+// it does so when a band's workgroups also fit on the current device at once
+// (rms_band_fits), else it runs the row-statistics kernel and the two-read
+// quantizer, with r after the control line.  The workspace is sized by K
+// alone, for the single-read layout where K allows it, which is the larger.
 static bool rms_single_read(int64_t K) { return K % 256 == 0 && K < ((int64_t)1 << 26); }
 
 size_t w8a8_rmsnorm_quantize_workspace_bytes(int64_t M, int64_t K) {
@@ -455,7 +457,8 @@ size_t w8a8_rmsnorm_quantize_workspace_bytes(int64_t M, int64_t K) {
 // Fused RMS producer into qx/sx with `ws` (device, 16-byte aligned, large enough).
 static hipError_t rms_quantize(const uint16_t *x, int64_t M, int64_t L, int64_t K, double eps, const uint16_t *scale,
                                const uint16_t *shift, void *ws, int8_t *qx, float *sx, hipStream_t stream) {
-    if (rms_single_read(K)) return w8a8::launch_rms_band_quantize(x, M, L, K, eps, scale, shift, ws, qx, sx, stream);
+    if (rms_single_read(K) && w8a8::rms_band_fits(K))
+        return w8a8::launch_rms_band_quantize(x, M, L, K, eps, scale, shift, ws, qx, sx, stream);
     float *r = reinterpret_cast<float *>(static_cast<char *>(ws) + kRmsCtrl);
     const hipError_t e = w8a8::launch_rms_rows(x, M, K, eps, r, stream);
     if (e != hipSuccess) return e;

@@ -62,9 +62,10 @@ hipError_t launch_modulate_quantize(const uint16_t *x, const float *stats, bool 
                                     int64_t K, const uint16_t *scale, const uint16_t *shift, int8_t *q, float *s,
                                     hipStream_t stream);
 // RMS form, single read of x (K % 256 == 0, K < 2^26, rows and K multiples of
-// 128).  Workspace, 16-byte aligned: a control line (word 0: nonzero if a
-// wait between workgroups gave up), one line per 128-row band holding its
-// arrival counter, then the fp64 row partials [rows / 128][K / 256][128].
+// 128; taken only where rms_band_fits(K)).  Workspace, 16-byte aligned: a
+// control line (word 0: nonzero if a wait between workgroups gave up), one
+// line per 128-row band holding its arrival counter, then the fp64 row
+// partials [rows / 128][K / 256][128].
 constexpr size_t kBandCtrlLine = 256;
 constexpr int64_t kBandCols = 256;
 inline size_t rms_band_workspace_bytes(int64_t rows, int64_t K) {
@@ -73,6 +74,10 @@ inline size_t rms_band_workspace_bytes(int64_t rows, int64_t K) {
 hipError_t launch_rms_band_quantize(const uint16_t *x, int64_t rows, int64_t L, int64_t K, double eps,
                                     const uint16_t *scale, const uint16_t *shift, void *workspace, int8_t *q,
                                     float *s, hipStream_t stream);
+// True when the current device can hold all K / 256 workgroups of a band
+// at once with half of its resident capacity for the band kernel to spare
+// (the band's workgroups wait for one another); false if the query fails.
+bool rms_band_fits(int64_t K);
 
 // bf16 fallback on the 256x256-tile kernel: x, w, y 16-byte aligned, K % 64 == 0,
 // K <= 2^21, N % 128 == 0, any M >= 1; bias 8-byte aligned or null.

@@ -288,9 +288,11 @@ size_t w8a8_rmsnorm_quantize_workspace_bytes(int64_t M, int64_t K);
  * applied to w8a8_rmsnorm_modulate_bf16's output).  B*L and K must be
  * multiples of 128 (else W8A8_ERR_UNSUPPORTED).
  *
- * When K % 256 == 0, x is read once: the workgroups of each 128-row band
- * hold 256-column slices in registers and exchange fp64 row partials through
- * the workspace, waiting for one another (bounded: a wait that does not
+ * When K % 256 == 0 and the K/256 workgroups of a band need at most half of
+ * what the current device holds of them at once (K up to 98304 on a whole
+ * MI355X), x is read once: the workgroups of each 128-row band hold
+ * 256-column slices in registers and exchange fp64 row partials through the
+ * workspace, waiting for one another (bounded: a wait that does not
  * complete in ~1 s gives up and leaves the codes of its slice wrong; the
  * workspace's first 32-bit word is cleared at the start of such a call and
  * set nonzero by a wait that gives up).  Other widths take two reads of x

@@ -55,6 +55,7 @@ hipError_t launch_rms_band_quantize(const uint16_t *, int64_t, int64_t, int64_t,
                                     const uint16_t *, void *, int8_t *, float *, hipStream_t) {
     reached("rms_band_quantize");
 }
+bool rms_band_fits(int64_t) { reached("rms_band_fits (a device query)"); }
 }  // namespace w8a8
 
 #define CHECK(cond)                                                                    \

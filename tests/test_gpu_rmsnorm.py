@@ -89,6 +89,24 @@ def test_single_read_workspace_reuse_and_error_word():
         print(f"rms single-read reuse {B}x{L}x{K}: equal to the unfused chain", flush=True)
 
 
+
+def test_band_larger_than_the_device_takes_two_reads():
+    """The workgroups of a band wait for one another, so a width whose band
+    cannot be resident at once (K = 2^20: 4096 workgroups per band, beyond
+    what any single device holds) must take the two-read path: the error word
+    keeps what the caller left there, and the codes and scales equal the
+    oracle's bit for bit."""
+    B, L, K = 1, 128, 1 << 20
+    x = random_bf16(700, (B * L, K), 2.0)
+    sc, sh = random_bf16(701, (B, K), 0.3), random_bf16(702, (B, K), 0.3)
+    ws = torch.empty(w8a8.rmsnorm_quantize_workspace_bytes(B * L, K), dtype=torch.uint8, device="cuda")
+    ws[:4].view(torch.int32).fill_(0x5A5A5A5A)
+    q, s = w8a8.rmsnorm_modulate_quantize_act(dev(x).view(B, L, K), dev(sc), dev(sh), 1e-6, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0x5A5A5A5A, "the single-read kernel ran"
+    oq, os_ = oracle.rmsnorm_modulate_quantize_block(x, L, sc, sh, 1e-6)
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+
 def test_zero_modulated_block_gives_zero_scale():
     # x = 0 and shift = 0: y = 0 in the whole block -> s = 0 and q = 0
     B, L, K = 1, 128, 256
