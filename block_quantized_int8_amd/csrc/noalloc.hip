@@ -51,8 +51,6 @@ extern "C" int w8a8_linear_noalloc(const void *x, int x_dtype, int64_t M, int64_
                                    const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
                                    hipStream_t stream, int *path_out) {
     if (!x || !w_bf16 || !y_bf16 || M <= 0 || K <= 0 || N <= 0) return W8A8_ERR_INVALID_ARG;
-    // the INT8 path's workspace must fit the array (0 for shapes that always fall back)
-    if (qw && w8a8_linear_workspace_bytes(M, K) > (size_t)W8A8_NOALLOC_SCRATCH_BYTES) return W8A8_ERR_UNSUPPORTED;
     int device = -1;
     hipError_t e = stream ? hipStreamGetDevice(stream, &device) : hipGetDevice(&device);
     if (e == hipSuccess && (device < 0 || device >= kMaxDevices)) e = hipErrorInvalidDevice;
@@ -62,6 +60,8 @@ extern "C" int w8a8_linear_noalloc(const void *x, int x_dtype, int64_t M, int64_
         (void)hipGetLastError();
         return w8a8::hip_failure(e);
     }
+    // a call whose INT8 path needs more than the array gets W8A8_ERR_UNSUPPORTED
+    // (the guard decides the path first, so a call that falls back runs)
     return w8a8::guarded_linear(x, x_dtype, M, K, N, w_bf16, qw, sw, bias_bf16, y_bf16, ws,
-                                W8A8_NOALLOC_SCRATCH_BYTES, stream, path_out);
+                                W8A8_NOALLOC_SCRATCH_BYTES, stream, path_out, W8A8_ERR_UNSUPPORTED);
 }

@@ -77,13 +77,14 @@ int guarded_path(int x_dtype, int64_t M, int64_t K, int64_t N, const void *x, co
     return path;
 }
 
-// Workspace checks of a call that takes the INT8 path: present, large
-// enough and device memory (else W8A8_ERR_INVALID_ARG); a workspace that is
-// not 16-byte aligned sends the call to the fallback instead.
+// Workspace checks of a call that takes the INT8 path: present and large
+// enough (else small_status), device memory (else W8A8_ERR_INVALID_ARG); a
+// workspace that is not 16-byte aligned sends the call to the fallback
+// instead.
 int int8_workspace(int &path, const int8_t *qw, const float *sw, void *workspace, size_t workspace_bytes,
-                   size_t need) {
+                   size_t need, int small_status = W8A8_ERR_INVALID_ARG) {
     if (path != W8A8_PATH_INT8) return W8A8_OK;
-    if (!workspace || workspace_bytes < need) return W8A8_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < need) return small_status;
     if (!is_device_ptr(qw) || !is_device_ptr(sw) || !is_device_ptr(workspace)) return W8A8_ERR_INVALID_ARG;
     if (!aligned(workspace, 16)) path = W8A8_PATH_BF16;
     return W8A8_OK;
@@ -138,7 +139,7 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, con
                 const int8_t *qw, const float *sw, const void *bias_bf16, void *y_bf16,
                 void *workspace, size_t workspace_bytes, hipStream_t stream, int *path_out) {
     return w8a8::guarded_linear(x, x_dtype, M, K, N, w_bf16, qw, sw, bias_bf16, y_bf16, workspace, workspace_bytes,
-                                stream, path_out);
+                                stream, path_out, W8A8_ERR_INVALID_ARG);
 }
 
 }  // extern "C"
@@ -147,7 +148,7 @@ namespace w8a8 {
 
 int guarded_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16, const int8_t *qw,
                    const float *sw, const void *bias_bf16, void *y_bf16, void *workspace, size_t workspace_bytes,
-                   hipStream_t stream, int *path_out) {
+                   hipStream_t stream, int *path_out, int small_workspace_status) {
     if (!x || !w_bf16 || !y_bf16 || M <= 0 || K <= 0 || N <= 0 || !valid_dtype(x_dtype))
         return W8A8_ERR_INVALID_ARG;
     if ((qw == nullptr) != (sw == nullptr)) return W8A8_ERR_INVALID_ARG;
@@ -157,7 +158,8 @@ int guarded_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, 
 
     // the INT8 kernels use 16-byte loads/stores: misaligned operands fall back
     int path = guarded_path(x_dtype, M, K, N, x, y_bf16, qw, sw, 4, bias_bf16, W8A8_BLOCK_MAX_K);
-    const int ws_status = int8_workspace(path, qw, sw, workspace, workspace_bytes, w8a8_linear_workspace_bytes(M, K));
+    const int ws_status = int8_workspace(path, qw, sw, workspace, workspace_bytes, w8a8_linear_workspace_bytes(M, K),
+                                         small_workspace_status);
     if (ws_status != W8A8_OK) return ws_status;
     if (path_out) *path_out = path;
 

@@ -90,9 +90,12 @@ int hip_failure(hipError_t e);
 
 // The body of w8a8_linear (guard, checks, launches) with the caller's
 // workspace; shared by the entry points that bring the workspace differently.
+// A call that takes the INT8 path with a workspace smaller than it needs
+// returns small_workspace_status (W8A8_ERR_INVALID_ARG for a caller's
+// workspace, W8A8_ERR_UNSUPPORTED for the library's fixed array).
 int guarded_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, const void *w_bf16, const int8_t *qw,
                    const float *sw, const void *bias_bf16, void *y_bf16, void *workspace, size_t workspace_bytes,
-                   hipStream_t stream, int *path_out);
+                   hipStream_t stream, int *path_out, int small_workspace_status);
 
 // x_dtype: 0 bf16, 1 fp16, 2 fp32 (the W8A8_DTYPE_* codes).
 hipError_t launch_gemm_bf16(const void *x, int x_dtype, const uint16_t *w, const uint16_t *bias,

@@ -144,8 +144,10 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t N, con
  * of W8A8_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
  * on until the process ends; this entry never allocates or frees memory.
  * Same guard, arguments, results and errors as w8a8_linear, plus:
- * W8A8_ERR_UNSUPPORTED when qw is given and w8a8_linear_workspace_bytes(M, K)
- * exceeds the array (use w8a8_linear with a caller workspace then);
+ * W8A8_ERR_UNSUPPORTED when the call takes the INT8 path and
+ * w8a8_linear_workspace_bytes(M, K) exceeds the array (use w8a8_linear with
+ * a caller workspace then; a call that the guard sends to the fallback runs
+ * at any size);
  * W8A8_ERR_HIP if the array's device address cannot be obtained.  The array
  * belongs to the stream's device (the current device for the null stream).
  * Calls share it: calls that overlap in time on one GPU (several streams,

@@ -3,7 +3,9 @@ against w8a8_linear, through the C ABI: two calls in a row, the second with
 a smaller input, each equal to w8a8_linear's output bit for bit (the same
 kernels on the same data; only where the workspace lives differs) and within
 the bf16 tolerance of the oracle; a fallback-routed shape; and the size
-limit of its fixed device array, rejected before anything is enqueued."""
+limit of its fixed device array, rejected before anything is enqueued when
+the INT8 path would need more, while a call the guard sends to the fallback
+runs at that size."""
 import ctypes
 
 import pytest
@@ -76,3 +78,14 @@ def test_noalloc_fallback_and_size_limit():
     st, path = _noalloc(xb, wb, None, None, None, yb)
     torch.cuda.synchronize()
     assert st == 0 and path == w8a8.PATH_BF16 and bool((yb == 0).all())
+    # the same size with qw but x 2 bytes off 16-byte alignment: the guard sends
+    # it to the fallback, which runs (the array's limit binds the INT8 path only)
+    g = torch.Generator(device="cuda").manual_seed(412)
+    xm = torch.randn(Mb * Kb + 1, generator=g, device="cuda").to(torch.bfloat16)[1:].view(Mb, Kb)
+    wm = (torch.randn((Nb, Kb), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    qm, sm = w8a8.quantize_weight(wm)
+    st, path = _noalloc(xm, wm, qm, sm, None, yb)
+    ref, ref_path = w8a8.linear(xm, wm, qm, sm)
+    torch.cuda.synchronize()
+    assert st == 0 and path == ref_path == w8a8.PATH_BF16
+    assert torch.equal(yb.view(torch.int16), ref.view(torch.int16))
