@@ -107,6 +107,35 @@ def test_band_larger_than_the_device_takes_two_reads():
     oq, os_ = oracle.rmsnorm_modulate_quantize_block(x, L, sc, sh, 1e-6)
     assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
 
+
+def test_single_read_on_two_streams_at_once():
+    """Two single-read launches in flight together on two streams (default
+    priority), each with its own workspace: K = 65536 gives 256 workgroups
+    per band, within the half of the device's capacity the router allows, so
+    both kernels' bands can be resident at once and neither wait gives up
+    (error words 0); each result equals the unfused chain bit for bit."""
+    B, L, K = 1, 512, 65536
+    xs, scs, shs, wss = [], [], [], []
+    for i in range(2):
+        xs.append(dev(random_bf16(710 + i, (B * L, K), 2.0)).view(B, L, K))
+        scs.append(dev(random_bf16(720 + i, (B, K), 0.3)))
+        shs.append(dev(random_bf16(730 + i, (B, K), 0.3)))
+        ws = torch.empty(w8a8.rmsnorm_quantize_workspace_bytes(B * L, K), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xA5)
+        wss.append(ws)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    for i in range(2):
+        with torch.cuda.stream(streams[i]):
+            outs[i] = w8a8.rmsnorm_modulate_quantize_act(xs[i], scs[i], shs[i], 1e-6, workspace=wss[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert int(wss[i][:4].view(torch.int32).item()) == 0, f"stream {i}: a wait gave up"
+        q2, s2 = w8a8.quantize_act(w8a8.rmsnorm_modulate_bf16(xs[i], scs[i], shs[i], 1e-6).view(B * L, K))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[i][0], q2) and torch.equal(outs[i][1], s2), i
+
 def test_zero_modulated_block_gives_zero_scale():
     # x = 0 and shift = 0: y = 0 in the whole block -> s = 0 and q = 0
     B, L, K = 1, 128, 256
